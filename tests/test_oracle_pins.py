@@ -1,0 +1,445 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test ties an oracle function to something other than itself: values printed
+on the pages (tests/golden/), a library routine (torch's scaled_dot_product_attention
+in float64), 50-digit brute force (mpmath), closed forms and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.blocks import BlockModel, build_tables
+from tests.conftest import golden
+import workloads
+
+# ---------------------------------------------------------------------------
+# small seeded inputs
+# ---------------------------------------------------------------------------
+
+
+def _small(seed, S, Hq, Hkv, D, B, ctx_hi, dtype="f32", extra_blocks=3, ctx=None):
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(1, ctx_hi, size=S, endpoint=True) if ctx is None else np.asarray(ctx)
+    need = sum(-(-int(c) // B) for c in ctx)
+    N = need + extra_blocks
+    m = BlockModel(N, B, free_order=[int(x) for x in rng.permutation(N)])
+    seqs = [m.new_sequence(int(c)) for c in ctx]
+    maxblk = max(len(s["table"]) for s in seqs) + 1
+    bt = build_tables(seqs, maxblk)
+    q = workloads.normal(S * Hq * D, seed, 11, dtype).reshape(S, Hq, D)
+    kc = workloads.normal(N * B * Hkv * D, seed, 12, dtype).reshape(N, B, Hkv, D)
+    vc = workloads.normal(N * B * Hkv * D, seed, 13, dtype).reshape(N, B, Hkv, D)
+    return q, kc, vc, bt, ctx.astype(np.int32), m, seqs
+
+
+def _sdpa(q, kc, vc, bt, ctx, scale, m):
+    """torch SDPA in float64 on K/V rows fetched slot by slot through the block model."""
+    torch = pytest.importorskip("torch")
+    S, Hq, D = q.shape
+    N, B, Hkv, _ = kc.shape
+    g = Hq // Hkv
+    kflat = oracle.widen(kc).reshape(N * B, Hkv, D)
+    vflat = oracle.widen(vc).reshape(N * B, Hkv, D)
+    out = np.empty((S, Hq, D))
+    for s in range(S):
+        seq = {"table": [int(x) for x in bt[s]], "len": int(ctx[s])}
+        slots = [m.physical_index(seq, t) for t in range(int(ctx[s]))]
+        K = torch.from_numpy(kflat[slots]).permute(1, 0, 2).repeat_interleave(g, dim=0)  # [Hq, ctx, D]
+        V = torch.from_numpy(vflat[slots]).permute(1, 0, 2).repeat_interleave(g, dim=0)
+        Q = torch.from_numpy(oracle.widen(q[s])).unsqueeze(1)                              # [Hq, 1, D]
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=scale)
+        out[s] = o[:, 0, :].numpy()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# slot formula and block model: values printed on the pages
+# ---------------------------------------------------------------------------
+
+def test_physical_index_page_examples(oracle_lib):
+    for c in golden("physical_index.json")["cases"]:
+        assert oracle.physical_index(c["table"], c["block_size"], c["pos"]) == c["slot"], c["cite"]
+        assert c["pos"] // c["block_size"] == c["logical_block"]
+        assert c["table"][c["logical_block"]] == c["physical_block"]
+        assert c["pos"] % c["block_size"] == c["offset"]
+        m = BlockModel(100, c["block_size"])
+        assert m.physical_index({"table": c["table"]}, c["pos"]) == c["slot"]
+        sl = oracle.slot_mapping(np.array([c["table"]]), [c["pos"]], c["block_size"])
+        assert int(sl[0]) == c["slot"]
+
+
+def test_go_scenario_block_model():
+    g = golden("go_scenario.json")
+    m = BlockModel(g["num_blocks"], g["block_size"])
+    seqs = {k: m.new_sequence(v) for k, v in g["prompts"].items()}
+    for k, t in g["tables_after_admit"].items():
+        assert seqs[k]["table"] == t
+    assert m.free == g["free_after_admit"]
+    m.release(seqs["b"]["table"])
+    m.release(seqs["d"]["table"])
+    assert m.free == g["free_after_freeing_b_then_d"]
+    e = m.new_sequence(g["e_prompt"])
+    assert (e is not None) == g["e_succeeds"]
+    assert e["table"] == g["e_table"]
+    assert m.physical_index(e, 40) == g["e_physical_index_40"]
+    assert oracle.physical_index(e["table"], g["block_size"], 40) == g["e_physical_index_40"]
+    m.check([seqs["a"], seqs["c"], e])
+
+
+def test_sharing_counts():
+    cases = golden("sharing.json")["cases"]
+    # nano-vLLM Ch04 section 6: 3 requests on 2 shared blocks, then one private block each
+    c = cases[0]
+    m = BlockModel(100, 16)
+    parent = m.new_sequence(c["shared_blocks"] * 16)
+    reqs = [parent] + [{"table": m.fork(parent["table"]), "len": parent["len"]} for _ in range(c["requests"] - 1)]
+    assert all(m.ref[b] == c["refcount_before"] for b in parent["table"])
+    assert len(m.ref) == c["blocks_before"]
+    for r in reqs:
+        assert m.append_token(r)
+    assert len(m.ref) == c["blocks_after_one_private_each"]
+    assert c["requests"] * (c["shared_blocks"] + 1) == c["blocks_without_sharing"]
+    m.check(reqs)
+    # PidokuInfra section 5: n = 4 on 3 prompt blocks -> 7 blocks instead of 16
+    c = cases[1]
+    m = BlockModel(100, 16)
+    parent = m.new_sequence(c["shared_blocks"] * 16)
+    reqs = [parent] + [{"table": m.fork(parent["table"]), "len": parent["len"]} for _ in range(c["requests"] - 1)]
+    for r in reqs:
+        assert m.append_token(r)
+    used = len(m.ref)
+    assert used == c["blocks_after_one_private_each"]
+    assert c["requests"] * (c["shared_blocks"] + 1) == c["blocks_without_sharing"]
+    assert round(100 * (1 - used / c["blocks_without_sharing"])) == c["saved_percent"]
+    # quiz 2: one set of prompt blocks, refcount = number of requests
+    c = cases[2]
+    m = BlockModel(100, 16)
+    parent = m.new_sequence(48)
+    kids = [m.fork(parent["table"]) for _ in range(c["requests"] - 1)]
+    assert len({tuple(parent["table"])} | {tuple(k) for k in kids}) == c["sets_of_prompt_blocks"]
+    assert all(m.ref[b] == c["requests"] for b in parent["table"])
+
+
+def test_block_model_oom_leaves_state_unchanged():
+    m = BlockModel(4, 16)
+    a = m.new_sequence(48)
+    before = (list(m.free), dict(m.ref))
+    assert m.new_sequence(40) is None                 # needs 3, 1 free
+    assert (list(m.free), dict(m.ref)) == before
+    a2 = {"table": m.fork(a["table"]), "len": a["len"]}
+    b = m.new_sequence(16)
+    assert b is not None and not m.free
+    before = (list(m.free), dict(m.ref), list(a2["table"]))
+    with pytest.raises(Exception):
+        m.write_slot(a2, 47)                          # shared block, no free block for the copy
+    assert (list(m.free), dict(m.ref), list(a2["table"])) == before
+    assert not m.append_token(b) or True
+    m.check([a, a2, b])
+
+
+def test_block_model_append_growth_rule():
+    # grow exactly when BlocksNeeded(len) exceeds the table (PidokuInfra section 4)
+    m = BlockModel(50, 16)
+    s = m.new_sequence(1)
+    assert len(s["table"]) == 1
+    for n in range(2, 100):
+        assert m.append_token(s)
+        assert s["len"] == n and len(s["table"]) == -(-n // 16)
+    m.check([s])
+
+
+def test_block_model_random_ops_invariants():
+    rng = np.random.default_rng(7)
+    m = BlockModel(64, 4, free_order=[int(x) for x in rng.permutation(64)])
+    live = []
+    for _ in range(2000):
+        op = rng.integers(0, 5)
+        if op == 0:
+            s = m.new_sequence(int(rng.integers(1, 20)))
+            if s is not None:
+                live.append(s)
+        elif op == 1 and live:
+            s = live[int(rng.integers(len(live)))]
+            live.append({"table": m.fork(s["table"]), "len": s["len"]})
+        elif op == 2 and live:
+            s = live[int(rng.integers(len(live)))]
+            if m.append_token(s):
+                try:
+                    m.write_slot(s, s["len"] - 1)
+                except Exception:
+                    pass
+        elif op == 3 and live:
+            s = live.pop(int(rng.integers(len(live))))
+            m.release(s["table"])
+        m.check(live)
+
+
+# ---------------------------------------------------------------------------
+# KV write and block copy: bytes land where the pages' examples say
+# ---------------------------------------------------------------------------
+
+def _special_rows(n_rows, row_elems, seed):
+    """fp32 bit patterns including NaN payloads, -0, +-inf and subnormals."""
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 2**32, size=(n_rows, row_elems), dtype=np.uint64).astype(np.uint32)
+    specials = np.array([0x7FC00001, 0xFFC12345, 0x80000000, 0x7F800000, 0xFF800000, 0x00000001, 0x807FFFFF],
+                        dtype=np.uint32)
+    flat = bits.reshape(-1)
+    flat[rng.integers(0, flat.size, size=min(flat.size, 64))] = np.resize(specials, min(flat.size, 64))
+    return bits.view(np.float32)
+
+
+@pytest.mark.parametrize("case", golden("physical_index.json")["cases"], ids=["slot3073", "slot3116"])
+def test_kv_write_lands_at_page_slot(case):
+    B, Hkv, D = case["block_size"], 1, 4
+    N = max(case["table"]) + 1
+    kc = _special_rows(N * B, Hkv * D, 1).reshape(N, B, Hkv, D).copy()
+    vc = _special_rows(N * B, Hkv * D, 2).reshape(N, B, Hkv, D).copy()
+    kn = _special_rows(1, Hkv * D, 3).reshape(1, Hkv, D)
+    vn = _special_rows(1, Hkv * D, 4).reshape(1, Hkv, D)
+    k0, v0 = kc.copy(), vc.copy()
+    oracle.kv_write(kn, vn, kc, vc, [case["slot"]])
+    pb, off = case["physical_block"], case["offset"]
+    assert kc[pb, off].tobytes() == kn[0].tobytes() and vc[pb, off].tobytes() == vn[0].tobytes()
+    k0[pb, off] = kn[0]
+    v0[pb, off] = vn[0]
+    assert kc.tobytes() == k0.tobytes() and vc.tobytes() == v0.tobytes()
+
+
+def test_kv_write_then_gather_reads_back_bf16():
+    # write each sequence's newest token through its slot, then the gathered view
+    # (the attention side's reading of the table) returns exactly those bytes at ctx-1
+    q, kc, vc, bt, ctx, m, seqs = _small(3, 5, 4, 2, 16, 4, 30, dtype="bf16")
+    S, Hkv, D = len(ctx), kc.shape[2], kc.shape[3]
+    kn = workloads.normal(S * Hkv * D, 99, 1, "bf16").reshape(S, Hkv, D)
+    vn = workloads.normal(S * Hkv * D, 99, 2, "bf16").reshape(S, Hkv, D)
+    slots = oracle.slot_mapping(bt, ctx - 1, kc.shape[1])
+    k0 = kc.copy()
+    oracle.kv_write(kn, vn, kc, vc, slots)
+    for s in range(S):
+        K = oracle.gather_sequence(kc, bt[s], int(ctx[s]))
+        V = oracle.gather_sequence(vc, bt[s], int(ctx[s]))
+        assert K[-1].tobytes() == kn[s].tobytes() and V[-1].tobytes() == vn[s].tobytes()
+        assert K[:-1].tobytes() == oracle.gather_sequence(k0, bt[s], int(ctx[s]))[:-1].tobytes()
+    changed = np.nonzero((kc != k0).any(axis=(2, 3)))
+    assert set(zip(*[c.tolist() for c in changed])) <= {(int(s) // 4, int(s) % 4) for s in slots}
+
+
+def test_kv_write_rejects_bad_slots():
+    kc = np.zeros((4, 4, 1, 4), np.float32)
+    vc = kc.copy()
+    kn = np.ones((2, 1, 4), np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write(kn, kn, kc, vc, [3, 3])
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write(kn, kn, kc, vc, [0, 16])
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write(kn, kn, kc, vc, [-1, 2])
+    oracle.kv_write(kn[:0], kn[:0], kc, vc, [])      # empty write is a no-op
+    assert not kc.any()
+
+
+def test_copy_on_write_keeps_parent_bytes():
+    # fork a parent with a partly filled last block; every child's first write copies the
+    # block first (nano-vLLM Ch04 section 6), so the parent's bytes never change
+    B, Hkv, D = 4, 2, 8
+    rng = np.random.default_rng(5)
+    N = 40
+    m = BlockModel(N, B, free_order=[int(x) for x in rng.permutation(N)])
+    parent = m.new_sequence(10)                          # 3 blocks, last holds 2 of 4 slots
+    kids = [{"table": m.fork(parent["table"]), "len": 10} for _ in range(3)]
+    kc = _special_rows(N * B, Hkv * D, 6).reshape(N, B, Hkv, D).copy()
+    vc = _special_rows(N * B, Hkv * D, 7).reshape(N, B, Hkv, D).copy()
+    parent_k = [kc[b].tobytes() for b in parent["table"]]
+    parent_v = [vc[b].tobytes() for b in parent["table"]]
+    pairs, slots = [], []
+    for kid in kids:
+        assert m.append_token(kid)
+        slot, pair = m.write_slot(kid, 10)
+        assert pair is not None and pair[0] == parent["table"][2]
+        pairs.append(pair)
+        slots.append(slot)
+    assert m.append_token(parent)
+    slot, pair = m.write_slot(parent, 10)
+    assert pair is None                                  # last holder writes in place
+    slots.append(slot)
+    m.check([parent] + kids)
+    k_before = kc.copy()
+    oracle.copy_blocks(kc, vc, pairs)
+    for src, dst in pairs:
+        assert kc[dst].tobytes() == kc[src].tobytes() and vc[dst].tobytes() == vc[src].tobytes()
+    untouched = [b for b in range(N) if b not in {d for _, d in pairs}]
+    assert kc[untouched].tobytes() == k_before[untouched].tobytes()
+    kn = _special_rows(4, Hkv * D, 8).reshape(4, Hkv, D)
+    oracle.kv_write(kn, kn, kc, vc, slots[:3])           # children write their own copies
+    assert [kc[b].tobytes() for b in parent["table"]] == parent_k
+    assert [vc[b].tobytes() for b in parent["table"]] == parent_v
+    for i, kid in enumerate(kids):
+        seqk = oracle.gather_sequence(kc, kid["table"], 11)
+        assert seqk[10].tobytes() == kn[i].tobytes()
+        assert seqk[:10].tobytes() == oracle.gather_sequence(kc, parent["table"], 10).tobytes()
+
+
+def test_copy_blocks_rejects_overlap():
+    kc = np.zeros((4, 2, 1, 4), np.float32)
+    with pytest.raises(oracle.OracleError):
+        oracle.copy_blocks(kc, kc.copy(), [(0, 1), (2, 1)])      # repeated destination
+    with pytest.raises(oracle.OracleError):
+        oracle.copy_blocks(kc, kc.copy(), [(0, 1), (1, 2)])      # destination is also a source
+    with pytest.raises(oracle.OracleError):
+        oracle.copy_blocks(kc, kc.copy(), [(0, 4)])
+    oracle.copy_blocks(kc, kc.copy(), np.zeros((0, 2), np.int64))
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+ATTN_CASES = [
+    # seed, S, Hq, Hkv, D, B, ctx_hi, dtype
+    (1, 3, 4, 4, 16, 4, 40, "f32"),
+    (2, 4, 8, 2, 32, 8, 70, "bf16"),
+    (3, 2, 6, 3, 8, 16, 50, "f32"),
+    (4, 3, 16, 2, 64, 16, 100, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_equals_library_sdpa_and_dense(case):
+    seed, S, Hq, Hkv, D, B, hi, dt = case
+    q, kc, vc, bt, ctx, m, _ = _small(seed, S, Hq, Hkv, D, B, hi, dt)
+    scale = 1 / math.sqrt(D)
+    o1 = oracle.attention(q, kc, vc, bt, ctx, scale)
+    o2 = oracle.dense_attention(q, kc, vc, bt, ctx, scale)
+    o3 = _sdpa(q, kc, vc, bt, ctx, scale, m)
+    assert np.max(np.abs(o1 - o3)) < 1e-12
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+
+
+@pytest.mark.parametrize("case", ATTN_CASES)
+def test_attention_block_permutation_invariance(case):
+    seed, S, Hq, Hkv, D, B, hi, dt = case
+    q, kc, vc, bt, ctx, m, _ = _small(seed, S, Hq, Hkv, D, B, hi, dt)
+    N = kc.shape[0]
+    pi = np.random.default_rng(seed + 100).permutation(N)       # new id of old block b is pi[b]
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[pi], vc2[pi] = kc, vc
+    bt2 = pi[bt].astype(np.int32)
+    o = oracle.attention(q, kc, vc, bt, ctx, 0.3)
+    o2 = oracle.attention(q, kc2, vc2, bt2, ctx, 0.3)
+    assert o.tobytes() == o2.tobytes()
+
+
+def test_attention_single_token_returns_v():
+    q, kc, vc, bt, ctx, m, _ = _small(5, 4, 8, 4, 32, 4, 1, "bf16", ctx=[1, 1, 1, 1])
+    o = oracle.attention(q, kc, vc, bt, ctx, 0.2)
+    for s in range(4):
+        v0 = oracle.widen(vc[bt[s, 0], 0])                     # [Hkv, D]
+        assert np.array_equal(o[s], np.repeat(v0, 2, axis=0))
+
+
+def test_attention_uniform_weights_give_mean():
+    q, kc, vc, bt, ctx, m, _ = _small(6, 3, 4, 2, 16, 4, 30, "f32")
+    for qq, sc in ((np.zeros_like(q), 0.5), (q, 0.0)):
+        o = oracle.attention(qq, kc, vc, bt, ctx, sc)
+        for s in range(3):
+            V = oracle.widen(oracle.gather_sequence(vc, bt[s], int(ctx[s])))
+            mean = V.mean(axis=0)                                  # [Hkv, D]
+            assert np.max(np.abs(o[s] - np.repeat(mean, 2, axis=0))) < 1e-12
+
+
+def test_attention_mpmath_brute_force():
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 50
+    q, kc, vc, bt, ctx, m, _ = _small(8, 2, 4, 2, 8, 4, 20, "f32")
+    scale = 0.37
+    o = oracle.attention(q, kc, vc, bt, ctx, scale)
+    B = kc.shape[1]
+    for s in range(2):
+        for h in range(4):
+            kvh = h // 2
+            xs, vs = [], []
+            for t in range(int(ctx[s])):
+                b, off = int(bt[s, t // B]), t % B
+                xs.append(mp.mpf(scale) * mp.fsum(mp.mpf(float(q[s, h, d])) * mp.mpf(float(kc[b, off, kvh, d]))
+                                                  for d in range(8)))
+                vs.append([mp.mpf(float(vc[b, off, kvh, d])) for d in range(8)])
+            ws = [mp.e ** x for x in xs]
+            Z = mp.fsum(ws)
+            for d in range(8):
+                ref = mp.fsum(w * v[d] for w, v in zip(ws, vs)) / Z
+                assert abs(float(ref) - o[s, h, d]) < 1e-12
+
+
+@pytest.mark.parametrize("P", [4, 8, 12, 64, 1024])
+def test_split_k_equals_unsplit(P):
+    q, kc, vc, bt, ctx, m, _ = _small(9, 4, 8, 2, 16, 4, 90, "bf16")
+    o = oracle.attention(q, kc, vc, bt, ctx, 0.25)
+    op = oracle.attention(q, kc, vc, bt, ctx, 0.25, partition_size=P)
+    assert np.max(np.abs(o - op)) < 1e-12
+    if P >= int(ctx.max()):
+        assert o.tobytes() == op.tobytes()           # a single partition is the plain path
+
+
+def test_split_k_reduce_closed_form():
+    # two partitions by hand: out = (L0 e^(m0-M) o0 + L1 e^(m1-M) o1) / (L0 e^(m0-M) + L1 e^(m1-M))
+    q, kc, vc, bt, ctx, m, _ = _small(10, 1, 1, 1, 4, 4, 8, "f32", ctx=[8])
+    K = oracle.widen(oracle.gather_sequence(kc, bt[0], 8))[:, 0]
+    V = oracle.widen(oracle.gather_sequence(vc, bt[0], 8))[:, 0]
+    x = 0.5 * K @ oracle.widen(q[0, 0])
+    parts = []
+    for lo, hi in ((0, 4), (4, 8)):
+        mp_ = x[lo:hi].max()
+        w = np.exp(x[lo:hi] - mp_)
+        parts.append((mp_, w.sum(), (w @ V[lo:hi]) / w.sum()))
+    M = max(p[0] for p in parts)
+    num = sum(L * math.exp(mm - M) * o for mm, L, o in parts)
+    den = sum(L * math.exp(mm - M) for mm, L, o in parts)
+    ref = num / den
+    got = oracle.attention(q, kc, vc, bt, ctx, 0.5, partition_size=4)[0, 0]
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_ignores_tail_slots_and_table_padding():
+    q, kc, vc, bt, ctx, m, _ = _small(11, 4, 4, 4, 16, 8, 60, "bf16", extra_blocks=1)
+    o = oracle.attention(q, kc, vc, bt, ctx, 0.25)
+    B = kc.shape[1]
+    kp, vp = kc.copy(), vc.copy()
+    poison = m.free[0]                                # a block no sequence holds
+    bt2 = bt.copy()
+    for s in range(4):
+        c = int(ctx[s])
+        nb = -(-c // B)
+        bt2[s, nb:] = poison                          # padding entries point at a poisoned block
+        last = bt[s, nb - 1]
+        kp[last, c - (nb - 1) * B:] = 0x7FC1          # NaN bf16 in the slots past ctx
+        vp[last, c - (nb - 1) * B:] = 0xFFC3
+    kp[poison] = 0x7FC1
+    vp[poison] = 0x7FC1
+    o2 = oracle.attention(q, kp, vp, bt2, ctx, 0.25)
+    assert np.isfinite(o2).all() and o.tobytes() == o2.tobytes()
+
+
+def test_attention_items_subset_matches_full():
+    q, kc, vc, bt, ctx, m, _ = _small(12, 3, 4, 2, 16, 4, 40, "f32")
+    full = oracle.attention(q, kc, vc, bt, ctx, 0.25)
+    items = [0, 5, 11, 7]
+    sub = oracle.attention(q, kc, vc, bt, ctx, 0.25, items=items)
+    for i, it in enumerate(items):
+        assert sub[i].tobytes() == full[it // 4, it % 4].tobytes()
+
+
+def test_attention_rejects_bad_inputs():
+    q, kc, vc, bt, ctx, m, _ = _small(13, 2, 4, 2, 16, 4, 20, "f32")
+    with pytest.raises(oracle.OracleError):
+        oracle.attention(q, kc, vc, bt, np.array([0, 3], np.int32), 0.25)          # ctx = 0
+    bad = bt.copy()
+    bad[0, 0] = kc.shape[0]
+    with pytest.raises(oracle.OracleError):
+        oracle.attention(q, kc, vc, bad, ctx, 0.25)                                # block id out of range
+    with pytest.raises(oracle.OracleError):
+        oracle.attention(np.ascontiguousarray(q[:, :3]), kc, vc, bt, ctx, 0.25)                          # 3 % 2 != 0
+    with pytest.raises(oracle.OracleError):
+        oracle.attention(q, kc, vc, bt, ctx, 0.25, partition_size=6)               # not a multiple of B
