@@ -1,0 +1,267 @@
+"""Decode-step benchmark of the paged KV cache path on one MI355X.
+
+One step = copy_blocks (copy-on-write pairs, when the step has any) ->
+paged_kv_write (each sequence's newest token) -> paged_attention_decode, over one
+synthetic batch already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload mha7b] [--only-main]
+
+The headline workload is the 7B-shaped MHA decode layer; the GQA, long-context and
+fork/copy-on-write workloads are measured in the same run and reported under
+"workloads".  Byte counts are algorithmic: what the method must move (K and V of
+every attended position once per KV head, q, out, block-table entries, lengths, and
+the written / copied rows), not what the implementation happens to move.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak), µs/decode step"
+HBM_PEAK_GBS = 8000.0
+# split-context partition used per workload (0 = one work unit per (sequence, KV head))
+PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 512, "long_splitk": 512, "fork_cow": 512}
+MAIN = "mha7b"
+
+
+def algorithmic_bytes(cfg, step) -> dict:
+    e = cfg.elem_bytes
+    S, Hq, Hkv, D, B = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    ctx = step.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * 2 * Hkv * D * e
+    attn = kv + 2 * S * Hq * D * e + 4 * int(sum(-(-int(c) // B) for c in ctx)) + 4 * S
+    T = len(step.slot_mapping)
+    write = 4 * T * Hkv * D * e + 8 * T
+    P = step.copy_pairs.shape[0]
+    copy = 2 * 2 * P * B * Hkv * D * e + 16 * P
+    return {"kv": kv, "attention": attn, "write": write, "copy": copy, "step": attn + write + copy}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_148_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, per_launch_alg: int):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int):
+    import torch
+    from paged_kv_cache_148_amd import batch, binding
+
+    cfg = workloads.CONFIGS[name]
+    t_gen = time.time()
+    wl = workloads.make_workload(cfg)
+    step = batch.step_for(wl, which)
+    bf16 = cfg.dtype == "bf16"
+    dev = "cuda"
+    q = batch.to_torch(wl.q, dev, bf16)
+    kc = batch.to_torch(wl.k_cache, dev, bf16)
+    vc = batch.to_torch(wl.v_cache, dev, bf16)
+    kn = batch.to_torch(wl.k_new, dev, bf16)
+    vn = batch.to_torch(wl.v_new, dev, bf16)
+    tables = batch.to_torch(step.block_tables, dev)
+    ctx = batch.to_torch(step.context_lens, dev)
+    slots = batch.to_torch(step.slot_mapping, dev)
+    pairs = batch.to_torch(step.copy_pairs, dev)
+    out = torch.empty_like(q)
+    ws_bytes = binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim, step.max_context_len,
+                                                partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t_gen
+    n_pairs = step.copy_pairs.shape[0]
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def one_step(i=None):
+        if n_pairs:
+            binding.copy_blocks(kc, vc, pairs)
+        binding.paged_kv_write(kn, vn, kc, vc, slots)
+        if i is not None:
+            ev[i][0].record()
+        binding.paged_attention_decode(out, q, kc, vc, tables, ctx, step.max_context_len, wl.scale, partition, ws)
+        if i is not None:
+            ev[i][1].record()
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one_step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / steps
+    attn_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    nb = algorithmic_bytes(cfg, step)
+    res = {
+        "workload": name, "step": which, "partition_size": partition,
+        "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
+        "attention_us_p10": attn_ms[len(attn_ms) // 10] * 1e3, "attention_us_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
+        "step_gbs": nb["step"] / step_s / 1e9,
+        "kv_gbs_attention": nb["kv"] / attn_s / 1e9,
+        "attention_alg_gbs": nb["attention"] / attn_s / 1e9,
+        "attention_hbm_frac": nb["attention"] / attn_s / 1e9 / HBM_PEAK_GBS,
+        "seqs_per_s": cfg.num_seqs / step_s,
+        "bytes": nb, "num_seqs": cfg.num_seqs, "sum_ctx": int(step.context_lens.sum()),
+        "max_ctx": int(step.max_context_len), "pool_blocks": wl.num_blocks,
+        "copy_pairs": int(n_pairs), "path": binding.attention_path(cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
+                                                                    cfg.block_size, 1 if bf16 else 0),
+        "input_gen_s": gen_s,
+    }
+    if name == "fork_cow":
+        shared = (cfg.ctx[1] // cfg.block_size) * cfg.block_size
+        unique_tokens = shared + int((step.context_lens.astype(np.int64) - shared).sum())
+        res["unique_kv_bytes"] = unique_tokens * 2 * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+        res["note"] = "unique KV fits the 256 MB Infinity Cache: logical GB/s is not an HBM figure"
+    del q, kc, vc, kn, vn, out, ws
+    torch.cuda.empty_cache()
+    return res, wl, step
+
+
+def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
+    """The CPU oracle on the same inputs: whole-step passes (copies, write, attention) on all
+    host cores, repeated until about budget_s seconds have been spent."""
+    import oracle
+    cfg = wl.cfg
+    nb = algorithmic_bytes(cfg, step)
+    reps, t_total = 0, 0.0
+    while reps == 0 or t_total < budget_s:
+        kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+        t = time.perf_counter()
+        oracle.copy_blocks(kc, vc, step.copy_pairs)
+        oracle.kv_write(wl.k_new, wl.v_new, kc, vc, step.slot_mapping)
+        oracle.attention(wl.q, kc, vc, step.block_tables, step.context_lens, wl.scale, partition)
+        t_total += time.perf_counter() - t
+        reps += 1
+        if reps >= 200:
+            break
+    per = t_total / reps
+    return {"value": nb["step"] / per / 1e9, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "us_per_step": per * 1e6,
+            "sample": f"{reps} whole decode step(s) of the {cfg.name} workload ({cfg.num_seqs} seqs, "
+                      f"{int(step.context_lens.sum())} tokens), fp64 scalar C + OpenMP, {t_total:.1f} s total",
+            "cpu": platform.processor() or _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=MAIN, choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--partition", type=int, default=None)
+    ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the decode path has no cross-GPU step in this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    main_part = PARTITION[args.workload] if args.partition is None else args.partition
+    which = "steady"
+    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part)
+    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step, attention {res['attention_us_mean']:.1f} us, "
+          f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
+    del wl
+    others = {}
+    if not args.only_main:
+        for name in ("gqa70b", "long_splitk", "fork_cow"):
+            if name == args.workload:
+                continue
+            for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
+                r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name])
+                others[f"{name}/{w}" if name == "fork_cow" else name] = r
+                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step, attention {r['attention_us_mean']:.1f} us,"
+                      f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+
+    cfg = workloads.CONFIGS[args.workload]
+    nb = res["bytes"]
+    traffic = measured_traffic(args.workload, nb["attention"])
+    line = {
+        "metric": METRIC,
+        "value": round(res["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["us_per_step"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded shuffled block pool)",
+        "config": {"workload": f"{args.workload}: {cfg.description}", "num_seqs": cfg.num_seqs,
+                   "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
+                   "block_size": cfg.block_size, "partition_size": main_part, "sum_ctx": res["sum_ctx"],
+                   "parallelism": "single GPU"},
+        "us_per_step": round(res["us_per_step"], 2),
+        "seqs_per_s": round(res["seqs_per_s"], 1),
+        "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attention_decode (attn_vec_kernel)" if res["path"] == 1 else
+                      "paged_attention_decode (attn_mfma_kernel)",
+            "achieved": round(res["attention_alg_gbs"], 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(res["attention_alg_gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": nb["attention"],
+            "launch_us_mean": round(res["attention_us_mean"], 2),
+        },
+        "cpu_baseline": cpu,
+        "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in others.items()},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

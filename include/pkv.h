@@ -1,0 +1,144 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV cache decode kernels for AMD MI355X (gfx950).
+ *
+ * The KV cache is one pre-allocated pool per tensor, split into num_blocks
+ * fixed-size physical blocks of block_size token slots; each sequence owns a
+ * block table mapping its logical blocks to physical block ids (pages
+ * "nano-vLLM . Ch04 . PagedAttention", section 4 "The Three Mechanisms", and
+ * "PagedAttention" (PidokuInfra, topic 10), section 5 "The kernel side").
+ *
+ * Layouts (row-major, element type given by pkv_dtype):
+ *   k_cache, v_cache : [num_blocks, block_size, num_kv_heads, head_dim]
+ *   q, out           : [num_seqs, num_heads, head_dim]
+ *   k_new, v_new     : [num_tokens, num_kv_heads, head_dim]
+ *   block_tables     : int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens     : int32 [num_seqs]
+ *   slot_mapping     : int64 [num_tokens], slot = block_id * block_size + offset
+ *   block_mapping    : int64 [num_pairs, 2], rows (src_block, dst_block)
+ *
+ * Ownership and threading: every array argument is a DEVICE pointer owned by the
+ * caller.  The library allocates nothing, keeps no state between calls and never
+ * synchronises: each call only enqueues kernels on `stream` (a hipStream_t; NULL
+ * is the default stream) and returns.  Calls are thread-safe.
+ *
+ * Errors: host-visible argument checks return a status before anything is
+ * enqueued (the pages' allocator reports failure by return value rather than by
+ * crashing; PidokuInfra section 4 ErrNoBlocks, nano-vLLM section 7).  A launch
+ * failure returns PKV_ERR_HIP.  Device-resident values cannot be checked on the
+ * host; how each kernel treats out-of-range device values is stated per call.
+ *
+ * Supported shapes: head_dim in {64, 128}; block_size in {4, 8, 16, 32};
+ * num_heads % num_kv_heads == 0; dtype fp32 or bf16.  Attention additionally
+ * needs g = num_heads / num_kv_heads <= 8, or g <= 16 on the bf16 matrix-core
+ * path (head_dim 128, block_size 16 or 32).  pkv_attention_path reports which.
+ * All data pointers must be 16-byte aligned, index arrays 4- or 8-byte aligned.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, workspace too small */
+  PKV_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, block_size, group size, dtype */
+  PKV_ERR_HIP = 3            /* the HIP runtime rejected a launch */
+} pkv_status;
+
+typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
+
+typedef enum { PKV_PATH_NONE = 0, PKV_PATH_VECTOR = 1, PKV_PATH_MFMA = 2 } pkv_path;
+
+/*
+ * paged_kv_write -- write the K/V rows of new tokens into the pool through a slot
+ * mapping computed on the host (nano-vLLM Ch04 section 4, Mechanism 3: slot =
+ * physical_block_id * block_size + offset_within_block; the kernel does no address
+ * translation of its own).  For token i with slot s, the bytes of k_new[i, :, :]
+ * land in k_cache[s / block_size, s % block_size, :, :], and likewise for V.  A bit
+ * copy: NaN payloads, -0 and subnormals are preserved; no other byte changes.
+ *
+ * Device values: slots outside [0, num_blocks * block_size) -- including the
+ * conventional -1 "no slot" -- are skipped (nothing is written for that token).
+ * Slots must be distinct within one call; with duplicates the result is undefined.
+ * num_tokens == 0 is a valid no-op.
+ */
+pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                          const int64_t *slot_mapping, int64_t num_tokens, int32_t num_blocks,
+                          int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                          void *stream);
+
+/*
+ * pkv_attention_workspace_size -- bytes of fp32 scratch that paged_attention_decode
+ * needs for its split-context partials, given the host-side maximum context length.
+ * 0 when partition_size == 0 or when no sequence can span more than one partition.
+ */
+size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pkv_attention_path -- which kernel family paged_attention_decode would run for these
+ * shapes (PKV_PATH_NONE if unsupported).
+ */
+pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            pkv_dtype dtype);
+
+/*
+ * paged_attention_decode -- one decode query per sequence:
+ *   out[s, h, :] = softmax(scale * q[s, h, :] . K_s^T) V_s
+ * where K_s, V_s are the rows of positions 0 .. context_lens[s]-1, position t living
+ * in physical block block_tables[s, t / block_size] at offset t % block_size
+ * (PidokuInfra section 5 "The kernel side": the walk over ceil(ctx / block_size)
+ * blocks through the table, with an online-softmax accumulation; tokentrails step 3:
+ * the same attention as on contiguous K/V).  Query head h reads KV head
+ * h / (num_heads / num_kv_heads).  Only positions < context_lens[s] are read: slots
+ * past it in the last block and table entries past ceil(ctx / block_size) are never
+ * touched.  Accumulation is fp32; out has the dtype of q.
+ *
+ * partition_size == 0: each (sequence, KV head) is one unit of work.  Otherwise
+ * (a multiple of block_size; a multiple of 16 on the MFMA path) the context is cut
+ * into partitions of that many tokens, partial softmax states go to `workspace`
+ * (at least pkv_attention_workspace_size bytes, 16-byte aligned) and a second kernel
+ * merges them by log-sum-exp in a fixed order, so results are deterministic.
+ * max_context_len must bound every context_lens[s] and fit the table
+ * (max_context_len <= max_blocks_per_seq * block_size); a sequence may span at most
+ * 8192 partitions (PKV_ERR_UNSUPPORTED beyond).
+ *
+ * Device values: context_lens[s] <= 0 gives out[s] = 0; context_lens[s] >
+ * max_context_len, or a table entry read that lies outside [0, num_blocks), gives
+ * NaN for the affected outputs.  Neither faults.
+ */
+pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                  const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t num_blocks, float scale, int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, pkv_dtype dtype, void *stream);
+
+/*
+ * copy_blocks -- the copy of copy-on-write (nano-vLLM Ch04 section 6: before a write
+ * into a block whose refcount is above one, copy the block first, then write;
+ * tokentrails Code box, copy_block).  For each row (src, dst) of block_mapping,
+ * the whole of physical block src -- all block_size slots -- is copied bit for bit
+ * into block dst, in k_cache and in v_cache.
+ *
+ * Device values: pairs with src or dst outside [0, num_blocks) are skipped.
+ * Destinations must be distinct and no destination may also be a source within
+ * one call; otherwise the result is undefined.  num_pairs == 0 is a valid no-op.
+ */
+pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, int64_t num_pairs,
+                       int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                       pkv_dtype dtype, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *pkv_status_string(pkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,177 @@
+"""Host-side block manager: the CPU bookkeeping that feeds the decode kernels.
+
+The pool of ``num_blocks`` physical blocks is handed out from a free stack; each
+sequence holds a block table (logical block -> physical id); a refcount per
+block allows sharing between forked sequences, with copy-on-write before a
+write into a shared block.  Sources:
+
+* page "nano-vLLM . Ch04 . PagedAttention": section 4 (free list, block table,
+  slot mapping computed on the CPU once per batch), section 6 (refcounts and
+  copy-on-write: copy first, drop the old block's count, hand the copy to the
+  writer, then write; with a count of one write in place), section 7
+  (allocation failure is a return value, not an exception).
+* page "PagedAttention" (PidokuInfra, topic 10), section 4: Allocate takes the
+  top n ids of the stack in stack order, Free returns an id when its count
+  reaches zero, Fork bumps every count, AppendToken grows the table by one block
+  when BlocksNeeded(len) exceeds its length, PhysicalIndex.
+
+Everything here is integer bookkeeping on the host; nothing is timed on the GPU.
+A failed allocation or copy-on-write leaves every structure unchanged.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass
+class Sequence:
+    """One request: its block table and its length in tokens."""
+    table: list = field(default_factory=list)
+    length: int = 0
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, free_order=None):
+        if num_blocks < 1 or block_size < 1:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        # free stack: the last element is handed out first; by default ids N-1..0 are
+        # pushed in that order, so id 0 is on top
+        if free_order is None:
+            self._free = list(range(num_blocks - 1, -1, -1))
+        else:
+            self._free = [int(b) for b in free_order]
+            if sorted(self._free) != list(range(num_blocks)):
+                raise ValueError("free_order must be a permutation of range(num_blocks)")
+        self._ref = np.zeros(num_blocks, dtype=np.int32)
+
+    # ------------------------------------------------------------------ pool
+    @property
+    def free_blocks(self) -> list:
+        return list(self._free)
+
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def refcount(self, block: int) -> int:
+        return int(self._ref[block])
+
+    def utilization(self) -> float:
+        """Fraction of the pool's blocks held by at least one sequence."""
+        return 1.0 - len(self._free) / self.num_blocks
+
+    def blocks_needed(self, tokens: int) -> int:
+        return -(-tokens // self.block_size)
+
+    def allocate(self, n: int):
+        """Pop n ids (top of the stack, in stack order) with refcount 1, or None if short."""
+        if n < 0:
+            raise ValueError("n must be >= 0")
+        if n > len(self._free):
+            return None
+        cut = len(self._free) - n
+        ids = self._free[cut:]
+        del self._free[cut:]
+        self._ref[ids] = 1
+        return ids
+
+    def free(self, blocks) -> None:
+        """Drop one reference to each block; a block returns to the stack at zero."""
+        for b in blocks:
+            if self._ref[b] <= 0:
+                raise ValueError(f"block {b} is not allocated")
+            self._ref[b] -= 1
+            if self._ref[b] == 0:
+                self._free.append(int(b))
+
+    def fork_table(self, blocks) -> list:
+        """Share the blocks with a new table (every refcount + 1)."""
+        for b in blocks:
+            if self._ref[b] <= 0:
+                raise ValueError(f"block {b} is not allocated")
+        for b in blocks:
+            self._ref[b] += 1
+        return list(blocks)
+
+    # ------------------------------------------------------------- sequences
+    def new_sequence(self, prompt_tokens: int):
+        ids = self.allocate(self.blocks_needed(prompt_tokens))
+        return None if ids is None else Sequence(ids, prompt_tokens)
+
+    def fork(self, seq: Sequence) -> Sequence:
+        return Sequence(self.fork_table(seq.table), seq.length)
+
+    def release(self, seq: Sequence) -> None:
+        self.free(seq.table)
+        seq.table = []
+        seq.length = 0
+
+    def append_token(self, seq: Sequence) -> bool:
+        """Grow the sequence by one token, taking one more block when it needs one."""
+        if self.blocks_needed(seq.length + 1) > len(seq.table):
+            ids = self.allocate(1)
+            if ids is None:
+                return False
+            seq.table.extend(ids)
+        seq.length += 1
+        return True
+
+    def physical_index(self, seq: Sequence, pos: int) -> int:
+        B = self.block_size
+        return seq.table[pos // B] * B + pos % B
+
+    def prepare_write(self, seq: Sequence, pos: int):
+        """Slot for writing position ``pos`` of ``seq``, applying copy-on-write.
+
+        Returns ``(slot, copy_pair)``; ``copy_pair`` is ``(src, dst)`` when the block was
+        shared and had to be copied to a fresh block first, else None.  Returns None
+        (and changes nothing) when a copy is needed but no block is free.
+        """
+        j = pos // self.block_size
+        old = seq.table[j]
+        if self._ref[old] > 1:
+            ids = self.allocate(1)
+            if ids is None:
+                return None
+            new = ids[0]
+            self._ref[old] -= 1
+            seq.table[j] = new
+            return self.physical_index(seq, pos), (old, new)
+        return self.physical_index(seq, pos), None
+
+    # ------------------------------------------------------------ batch views
+    def slot_mapping(self, seqs, positions) -> np.ndarray:
+        """int64 slots of one batch: slot_i = table_i[pos_i // B] * B + pos_i % B."""
+        B = self.block_size
+        pos = np.asarray(positions, dtype=np.int64)
+        phys = np.array([s.table[p // B] for s, p in zip(seqs, pos.tolist())], dtype=np.int64)
+        return phys * B + pos % B
+
+    @staticmethod
+    def block_tables(seqs, max_blocks: int | None = None, pad: int = 0) -> np.ndarray:
+        """int32 [len(seqs), max_blocks] table rows, padded with ``pad``."""
+        width = max(len(s.table) for s in seqs) if max_blocks is None else max_blocks
+        out = np.full((len(seqs), width), pad, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            if len(s.table) > width:
+                raise ValueError("table longer than max_blocks")
+            out[i, :len(s.table)] = s.table
+        return out
+
+    def check(self, seqs) -> None:
+        """Invariants: each refcount equals the number of tables holding the block; a block
+        is on the free stack exactly when its refcount is zero; the stack has no repeats."""
+        counts = np.zeros(self.num_blocks, dtype=np.int64)
+        for s in seqs:
+            np.add.at(counts, np.asarray(s.table, dtype=np.int64), 1)
+        if not np.array_equal(counts, self._ref):
+            raise AssertionError("refcounts do not match the tables")
+        free = np.zeros(self.num_blocks, dtype=bool)
+        free[self._free] = True
+        if len(set(self._free)) != len(self._free):
+            raise AssertionError("free stack holds a block twice")
+        if not np.array_equal(free, self._ref == 0):
+            raise AssertionError("free stack and zero refcounts disagree")

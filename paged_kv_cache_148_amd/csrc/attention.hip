@@ -1,0 +1,635 @@
+// attention.hip -- paged decode attention for gfx950 (CDNA4).
+//
+// For every sequence s and query head h:
+//   out[s,h] = softmax(scale * q[s,h] . K_s^T) V_s,
+// K_s / V_s being the rows of positions 0..ctx-1, position t stored in physical block
+// table[s][t / B] at offset t % B of the pool [N, B, Hkv, D].  The kernels walk the
+// block table and accumulate with an online softmax (page "PagedAttention",
+// PidokuInfra topic 10, section 5 "The kernel side"); the result is the ordinary
+// attention over the gathered rows (page "PagedAttention", tokentrails, step 3).
+//
+// Work unit: one workgroup (4 waves) per (context partition, KV head, sequence).  It
+// serves every query head of the KV head's group, so each K/V byte is read once per
+// group.  Without a partition size the partition is the whole context.  With one,
+// each workgroup leaves a partial state (running max m, sum l, unnormalised o) in the
+// workspace and attn_reduce_kernel merges the partials by log-sum-exp.  Sequences
+// whose context fits one partition are finished in pass 1.
+//
+// Two pass-1 kernels:
+//   attn_mfma_kernel  (bf16, D = 128, B % 16 == 0, 2 <= g <= 16): a 16-token tile of
+//     K times the group's Q^T on v_mfma_f32_16x16x32_bf16 gives the score tile; the
+//     probabilities stay in the MFMA result layout and feed v_mfma_f32_16x16x16_bf16
+//     against V^T for P.V.  The head dimension of the P.V product is permuted so that
+//     each lane's V operand is one 16-byte row piece of 4 tokens, regrouped in
+//     registers (no LDS round trip for V).
+//   attn_vec_kernel   (everything else: g = 1, fp32, D = 64, small blocks): one token
+//     row per D*e/16 lanes, 16-byte loads along head_dim, q.k by packed bf16 dot
+//     products or fp32 FMAs, row sums by DPP.
+// Scores carry scale * log2(e) so every exponential is a hardware exp2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_device.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
+
+struct AttnArgs {
+  void *out;
+  const void *q;
+  const void *k;
+  const void *v;
+  const int32_t *tables;
+  const int32_t *ctx;
+  float *ws_o;       // [S, Hq, max_parts, D]
+  float *ws_m;       // [S, Hq, max_parts]   log2-domain running max
+  float *ws_l;       // [S, Hq, max_parts]
+  int max_blocks;    // table row length
+  int max_ctx;       // host bound on ctx
+  int Hq, Hkv, g, N;
+  int P;             // partition length in tokens (whole context when not splitting)
+  int max_parts;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Merge weight of a partial state with max m into a combined max M (empty state -> 0).
+__device__ __forceinline__ float merge_weight(float m, float M) { return m == kNegInf ? 0.f : fast_exp2(m - M); }
+
+template <typename T>
+__device__ __forceinline__ void store_out(void *out, size_t idx, float v) {
+  if constexpr (sizeof(T) == 4)
+    reinterpret_cast<float *>(out)[idx] = v;
+  else
+    reinterpret_cast<uint16_t *>(out)[idx] = f32_to_bf16(v);
+}
+
+// Outputs of a sequence whose length is unusable: 0 for ctx <= 0, NaN for ctx above
+// the host bound.
+template <typename T, int D>
+__device__ void fill_group(const AttnArgs &a, int s, int h0, int g, float v) {
+  for (int i = threadIdx.x; i < g * D; i += blockDim.x) store_out<T>(a.out, ((size_t)s * a.Hq + h0) * D + i, v);
+}
+
+// Final phase of pass 1, shared by both kernels: the per-wave states (sm_m, sm_l,
+// sm_o) are merged, then either normalised into `out` or stored as a partial.
+template <typename T, int D, int GS, int OSTRIDE>
+__device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, int p, bool single,
+                                             const float (*sm_m)[GS], const float (*sm_l)[GS],
+                                             const float (*sm_o)[GS][OSTRIDE], const int *sm_bad) {
+  const int g = a.g;
+  const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
+  for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
+    const int j = idx / D, d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = merge_weight(sm_m[w][j], M);
+      L += wt * sm_l[w][j];
+      o += wt * sm_o[w][j][d];
+    }
+    if (bad) {
+      M = 0.f;
+      L = __builtin_nanf("");
+      o = __builtin_nanf("");
+    }
+    const int h = kvh * g + j;
+    if (single) {
+      store_out<T>(a.out, ((size_t)s * a.Hq + h) * D + d, o / L);
+    } else {
+      const size_t part = ((size_t)s * a.Hq + h) * a.max_parts + p;
+      a.ws_o[part * D + d] = o;
+      if (d == 0) {
+        a.ws_m[part] = M;
+        a.ws_l[part] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA path: bf16, D = 128, B in {16, 32}, group of up to 16 query heads.
+//
+// Lane l of a wave: c16 = l % 16, grp = l / 16.
+//   QK  (v_mfma_f32_16x16x32_bf16, A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]):
+//       lane l loads token c16's d-slice 32c + 8grp .. +7 for c = 0..3 and the same
+//       slice of head c16's q row.  Result S^T: lane l holds tokens 4grp + r (r = 0..3)
+//       of head c16.
+//   P.V (v_mfma_f32_16x16x16_bf16, A = V^T [16 d-rows x 16 tokens], B = P^T [16 tokens x
+//       16 heads]): B is exactly the S^T result layout (head c16, tokens 4grp + r).  MFMA
+//       number i (0..7) gives A-row c16 the head-dim index 8*c16 + i, so lane l needs
+//       d = 8*c16 .. 8*c16+7 of tokens 4grp + r: one 16-byte load per token, regrouped
+//       into (token pair, d) halves with byte permutes.  The accumulator of MFMA i holds,
+//       in lane l, row 4grp + r' -> d = 32*grp + 8*r' + i of head c16.
+// ---------------------------------------------------------------------------
+template <int B>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int OS = D + 4;   // padded head stride in LDS
+  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, grp = lane >> 4;
+  const int g = a.g;
+
+  __shared__ float sm_o[kWaves][16][OS];
+  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+  __shared__ int sm_bad[kWaves];
+
+  const int ctx = a.ctx[s];
+  if (ctx < 1 || ctx > a.max_ctx) {
+    if (p == 0) fill_group<uint16_t, D>(a, s, kvh * g, g, ctx < 1 ? 0.f : __builtin_nanf(""));
+    return;
+  }
+  const int t0 = p * a.P;
+  if (t0 >= ctx) return;
+  const int t1 = min(t0 + a.P, ctx);
+  const bool single = ctx <= a.P;
+
+  // Q^T operand: head c16 of the group (zero columns past g).
+  bf16x8 qop[4];
+  {
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + ((size_t)s * a.Hq + kvh * g + c16) * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (c16 < g) v = ld16(qrow + 32 * c + 8 * grp);
+      qop[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  float m = kNegInf, lsum = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int bad = 0;
+
+  const int32_t *table = a.tables + (size_t)s * a.max_blocks;
+  const size_t tok_stride = (size_t)a.Hkv * D;   // elements between consecutive slots
+  const uint16_t *kpool = reinterpret_cast<const uint16_t *>(a.k) + (size_t)kvh * D;
+  const uint16_t *vpool = reinterpret_cast<const uint16_t *>(a.v) + (size_t)kvh * D;
+  const uint32_t k_off = (uint32_t)(c16 * tok_stride + 8 * grp);
+  const uint32_t v_off = (uint32_t)(4 * grp * tok_stride + 8 * c16);
+
+  const int tile_hi = (t1 + 15) >> 4;
+  for (int tile = (t0 >> 4) + wave; tile < tile_hi; tile += kWaves) {
+    const int tok0 = tile << 4;
+    int phys = __builtin_amdgcn_readfirstlane(table[tok0 / B]);
+    if ((unsigned)phys >= (unsigned)a.N) {
+      bad = 1;
+      phys = 0;
+    }
+    const size_t base = ((size_t)phys * B + (tok0 % B)) * tok_stride;
+    const uint16_t *kb = kpool + base + k_off;
+    const uint16_t *vb = vpool + base + v_off;
+    u32x4 kr[4], vr[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kr[c] = ld16(kb + 32 * c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = ld16(vb + r * tok_stride);
+
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qop[c], sc, 0, 0, 0);
+
+    // scores of tokens tok0 + 4grp + r for head c16; positions past the end are masked
+    float sv[4], mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool ok = tok0 + 4 * grp + r < t1;
+      sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
+      if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = merge_weight(m, mnew);
+    float pr[4], ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - mnew);
+      ps += pr[r];
+    }
+    lsum = lsum * alpha + ps;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    }
+    m = mnew;
+
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+    const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int w = i >> 1;
+      uint32_t a01, a23;
+      if (i & 1) {
+        a01 = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
+        a23 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
+      } else {
+        a01 = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
+        a23 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
+      }
+      const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[i], 0, 0, 0);
+    }
+  }
+
+  float lh = lsum + __shfl_xor(lsum, 16);
+  lh += __shfl_xor(lh, 32);
+  if (grp == 0) {
+    sm_m[wave][c16] = m;
+    sm_l[wave][c16] = lh;
+  }
+  if (lane == 0) sm_bad[wave] = bad;
+  {
+    float *dst = &sm_o[wave][c16][32 * grp];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
+    }
+  }
+  __syncthreads();
+  finish_group<uint16_t, D, 16, OS>(a, s, kvh, p, single, sm_m, sm_l, sm_o, sm_bad);
+}
+
+// ---------------------------------------------------------------------------
+// Vector path.  T = float or uint16_t (bf16).  Each token row of a KV head is
+// D*sizeof(T) bytes = LPT lanes x 16 bytes; a wave covers TPW = 64 / LPT rows at once.
+// Lane l: row = l / LPT, column chunk cl = l % LPT -> elements cl*EPL .. +EPL-1.
+// Every row keeps its own online-softmax state; rows and waves are merged at the end.
+// The wave's unit of work is CH = max(B, TPW) consecutive tokens (STEPS row steps).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int G, int B>
+__global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
+  constexpr int EPL = 16 / (int)sizeof(T);
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = 64 / LPT;
+  constexpr int CH = B >= TPW ? B : TPW;
+  constexpr int STEPS = CH / TPW;
+  constexpr int OS = D + 4;
+  constexpr bool kBF16 = sizeof(T) == 2;
+  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane / LPT, cl = lane % LPT;
+  const int g = a.g;
+
+  __shared__ float sm_o[kWaves][G][OS];
+  __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
+  __shared__ int sm_bad[kWaves];
+
+  const int ctx = a.ctx[s];
+  if (ctx < 1 || ctx > a.max_ctx) {
+    if (p == 0) fill_group<T, D>(a, s, kvh * g, g, ctx < 1 ? 0.f : __builtin_nanf(""));
+    return;
+  }
+  const int t0 = p * a.P;
+  if (t0 >= ctx) return;
+  const int t1 = min(t0 + a.P, ctx);
+  const bool single = ctx <= a.P;
+
+  // this lane's slice of every query head in the group
+  u32x4 qraw[G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    qraw[j] = (u32x4){0u, 0u, 0u, 0u};
+    if (j < g) qraw[j] = ld16(reinterpret_cast<const T *>(a.q) + ((size_t)s * a.Hq + kvh * g + j) * D + cl * EPL);
+  }
+
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[j][e] = 0.f;
+  }
+  int bad = 0;
+
+  const int32_t *table = a.tables + (size_t)s * a.max_blocks;
+  const size_t tok_stride = (size_t)a.Hkv * D;
+  const T *kpool = reinterpret_cast<const T *>(a.k) + (size_t)kvh * D + cl * EPL;
+  const T *vpool = reinterpret_cast<const T *>(a.v) + (size_t)kvh * D + cl * EPL;
+
+  const int u_hi = (t1 + CH - 1) / CH;
+  for (int u = t0 / CH + wave; u < u_hi; u += kWaves) {
+    const int tokc = u * CH;
+    u32x4 kr[STEPS], vr[STEPS];
+    bool ok[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      const int t = tokc + st * TPW + row;
+      ok[st] = t >= t0 && t < t1;
+      int phys = 0;
+      if constexpr (B >= TPW) {
+        // the unit is one block and starts inside [t0, t1): its table entry is in use
+        phys = __builtin_amdgcn_readfirstlane(table[tokc / B]);
+      } else {
+        // the unit spans several blocks: only positions in [t0, t1) consult the table
+        if (ok[st]) phys = table[t / B];
+      }
+      if ((unsigned)phys >= (unsigned)a.N) {
+        bad = 1;
+        phys = 0;
+      }
+      const size_t off = ((size_t)phys * B + (t % B)) * tok_stride;
+      kr[st] = ld16(kpool + off);
+      vr[st] = ld16(vpool + off);
+      if (!ok[st]) vr[st] = (u32x4){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      if (j >= g) break;
+      float sc[STEPS];
+      float mx = kNegInf;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        float part = 0.f;
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[st][w]),
+                                                   __builtin_bit_cast(bf16x2, qraw[j][w]), part, false);
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) part = fmaf(__uint_as_float(kr[st][w]), __uint_as_float(qraw[j][w]), part);
+        }
+        part = group_sum<LPT>(part);
+        sc[st] = ok[st] ? part * a.scale_log2 : kNegInf;
+        mx = fmaxf(mx, sc[st]);
+      }
+      const float mnew = fmaxf(m[j], mx);
+      const float alpha = mnew == kNegInf ? 1.f : merge_weight(m[j], mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        sc[st] = sc[st] == kNegInf ? 0.f : fast_exp2(sc[st] - mnew);
+        ps += sc[st];
+      }
+      l[j] = l[j] * alpha + ps;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[j][e] *= alpha;
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st) {
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            o[j][2 * w] = fmaf(sc[st], bf16_lo(vr[st][w]), o[j][2 * w]);
+            o[j][2 * w + 1] = fmaf(sc[st], bf16_hi(vr[st][w]), o[j][2 * w + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) o[j][w] = fmaf(sc[st], __uint_as_float(vr[st][w]), o[j][w]);
+        }
+      }
+      m[j] = mnew;
+    }
+  }
+
+  // merge the TPW rows of the wave (butterfly over the row bits of the lane id)
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float m2 = __shfl_xor(m[j], off), l2 = __shfl_xor(l[j], off);
+      const float M = fmaxf(m[j], m2);
+      const float w1 = M == kNegInf ? 0.f : merge_weight(m[j], M);
+      const float w2 = M == kNegInf ? 0.f : merge_weight(m2, M);
+      l[j] = w1 * l[j] + w2 * l2;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float o2 = __shfl_xor(o[j][e], off);
+        o[j][e] = w1 * o[j][e] + w2 * o2;
+      }
+      m[j] = M;
+    }
+  }
+  if (row == 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sm_o[wave][j][cl * EPL + e] = o[j][e];
+      if (cl == 0) {
+        sm_m[wave][j] = m[j];
+        sm_l[wave][j] = l[j];
+      }
+    }
+  }
+  if (lane == 0) sm_bad[wave] = bad;
+  __syncthreads();
+  finish_group<T, D, G, OS>(a, s, kvh, p, single, sm_m, sm_l, sm_o, sm_bad);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: merge the partials of one (sequence, head):
+//   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p l_p.
+// The partition -> thread assignment and the reduction trees are fixed, so the result
+// does not depend on timing.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float *red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
+  __syncthreads();
+  return r;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a) {
+  constexpr int CHK = D / 4;            // float4 chunks per row
+  constexpr int PL = kThreads / CHK;    // partitions processed side by side
+  extern __shared__ float sm_w[];       // [max_parts] merge weights
+  __shared__ f32x4 sm_acc[kThreads];
+  __shared__ float red[kWaves];
+  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const int ctx = a.ctx[s];
+  if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
+  const int np = (ctx + a.P - 1) / a.P;
+  const size_t base = ((size_t)s * a.Hq + h) * a.max_parts;
+
+  float mx = kNegInf;
+  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, a.ws_m[base + i]);
+  const float M = block_reduce(mx, true, red);
+  float ls = 0.f;
+  for (int i = tid; i < np; i += kThreads) {
+    const float w = merge_weight(a.ws_m[base + i], M);
+    sm_w[i] = w;
+    ls += w * a.ws_l[base + i];
+  }
+  const float L = block_reduce(ls, false, red);   // its barriers also publish sm_w
+
+  const int c = tid % CHK, pl = tid / CHK;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.ws_o + base * D) + c;
+#pragma unroll 4
+  for (int i = pl; i < np; i += PL) acc += sm_w[i] * po[(size_t)i * CHK];
+  sm_acc[tid] = acc;
+  __syncthreads();
+  if (pl == 0) {
+#pragma unroll
+    for (int q = 1; q < PL; ++q) acc += sm_acc[q * CHK + c];
+    const size_t o = ((size_t)s * a.Hq + h) * D + 4 * c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out<T>(a.out, o + e, acc[e] / L);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static int vec_group(int g) { return g <= 1 ? 1 : g <= 2 ? 2 : g <= 4 ? 4 : g <= 8 ? 8 : 0; }
+
+static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PKV_PATH_NONE;
+  if (dt != PKV_DTYPE_F32 && dt != PKV_DTYPE_BF16) return PKV_PATH_NONE;
+  if (D != 64 && D != 128) return PKV_PATH_NONE;
+  if (B != 4 && B != 8 && B != 16 && B != 32) return PKV_PATH_NONE;
+  const int g = Hq / Hkv;
+  if (dt == PKV_DTYPE_BF16 && D == 128 && (B == 16 || B == 32) && g >= 2 && g <= 16) return PKV_PATH_MFMA;
+  return vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
+}
+
+template <typename T, int D, int G>
+static void launch_vec_b(dim3 grid, hipStream_t st, const AttnArgs &a, int B) {
+  switch (B) {
+    case 4: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 4>), grid, dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 8>), grid, dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 16>), grid, dim3(kThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 32>), grid, dim3(kThreads), 0, st, a); break;
+  }
+}
+
+template <typename T, int D>
+static void launch_vec(dim3 grid, hipStream_t st, const AttnArgs &a, int B) {
+  switch (vec_group(a.g)) {
+    case 1: launch_vec_b<T, D, 1>(grid, st, a, B); break;
+    case 2: launch_vec_b<T, D, 2>(grid, st, a, B); break;
+    case 4: launch_vec_b<T, D, 4>(grid, st, a, B); break;
+    default: launch_vec_b<T, D, 8>(grid, st, a, B); break;
+  }
+}
+
+template <typename T, int D>
+static void launch_reduce(dim3 grid, hipStream_t st, const AttnArgs &a) {
+  hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kThreads), (size_t)a.max_parts * sizeof(float), st, a);
+}
+
+static int64_t parts_for(int64_t max_ctx, int64_t P) { return (max_ctx + P - 1) / P; }
+
+static bool aligned(const void *p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) == 0; }
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, pkv_dtype dtype) {
+  return select_path(num_heads, num_kv_heads, head_dim, block_size, dtype);
+}
+
+extern "C" size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t partition_size) {
+  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int64_t np = parts_for(max_context_len, partition_size);
+  if (np <= 1) return 0;
+  return (size_t)num_seqs * num_heads * np * (head_dim + 2) * sizeof(float);
+}
+
+extern "C" pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_blocks, float scale,
+                                             int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                             pkv_dtype dtype, void *stream) {
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || max_context_len < 1 || partition_size < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
+  const pkv_path path = select_path(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  if (path == PKV_PATH_NONE) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_INVALID_ARG;
+  if (partition_size > 0 && partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_INVALID_ARG;
+  if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+
+  const int64_t P = partition_size > 0 ? partition_size : ((int64_t)max_context_len + 15) / 16 * 16;
+  const int64_t np = parts_for(max_context_len, P);
+  if (np > 1) {
+    if (np > kMaxReduceParts) return PKV_ERR_UNSUPPORTED;
+    const size_t need = pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
+  }
+
+  AttnArgs a;
+  a.out = out;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.ctx = context_lens;
+  const size_t nparts_total = (size_t)num_seqs * num_heads * (size_t)np;
+  a.ws_o = np > 1 ? reinterpret_cast<float *>(workspace) : nullptr;
+  a.ws_m = np > 1 ? a.ws_o + nparts_total * head_dim : nullptr;
+  a.ws_l = np > 1 ? a.ws_m + nparts_total : nullptr;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_ctx = max_context_len;
+  a.Hq = num_heads;
+  a.Hkv = num_kv_heads;
+  a.g = num_heads / num_kv_heads;
+  a.N = num_blocks;
+  a.P = (int)P;
+  a.max_parts = (int)np;
+  a.scale_log2 = scale * kLog2e;
+
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid((unsigned)np, (unsigned)num_kv_heads, (unsigned)num_seqs);
+  const bool bf16 = dtype == PKV_DTYPE_BF16;
+  if (path == PKV_PATH_MFMA) {
+    if (block_size == 16)
+      hipLaunchKernelGGL((attn_mfma_kernel<16>), grid, dim3(kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<32>), grid, dim3(kThreads), 0, st, a);
+  } else if (bf16) {
+    if (head_dim == 128) launch_vec<uint16_t, 128>(grid, st, a, block_size);
+    else launch_vec<uint16_t, 64>(grid, st, a, block_size);
+  } else {
+    if (head_dim == 128) launch_vec<float, 128>(grid, st, a, block_size);
+    else launch_vec<float, 64>(grid, st, a, block_size);
+  }
+  if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  if (np > 1) {
+    const dim3 rgrid((unsigned)num_heads, (unsigned)num_seqs);
+    if (bf16) {
+      if (head_dim == 128) launch_reduce<uint16_t, 128>(rgrid, st, a);
+      else launch_reduce<uint16_t, 64>(rgrid, st, a);
+    } else {
+      if (head_dim == 128) launch_reduce<float, 128>(rgrid, st, a);
+      else launch_reduce<float, 64>(rgrid, st, a);
+    }
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}

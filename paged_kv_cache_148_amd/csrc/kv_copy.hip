@@ -1,0 +1,130 @@
+// kv_copy.hip -- the two data-movement kernels of the paged KV cache:
+//   paged_kv_write: new tokens' K/V rows into the pool through a host-built slot mapping
+//                   (nano-vLLM Ch04, section 4 "The Three Mechanisms", Mechanism 3);
+//   copy_blocks:    whole-block copies for copy-on-write (nano-vLLM Ch04, section 6).
+// Both are pure 16-byte integer moves, so every bit pattern (NaN payloads, -0,
+// subnormals) survives.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+#include "pkv_device.h"
+
+namespace pkv {
+
+// One workgroup per token (grid-stride beyond the grid).  A slot names one
+// [Hkv, D] row of the pool; consecutive slots are consecutive rows, so the row of
+// slot s = b * B + o starts s * row_vecs 16-byte vectors into the pool.
+__global__ __launch_bounds__(256) void kv_write_kernel(const u32x4 *__restrict__ k_new,
+                                                       const u32x4 *__restrict__ v_new,
+                                                       u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
+                                                       const int64_t *__restrict__ slots, int64_t num_tokens,
+                                                       int row_vecs, int64_t num_slots) {
+  for (int64_t tok = blockIdx.x; tok < num_tokens; tok += gridDim.x) {
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= num_slots) continue;  // -1 / out of range: no write
+    const u32x4 *ks = k_new + tok * row_vecs;
+    const u32x4 *vs = v_new + tok * row_vecs;
+    u32x4 *kd = k_cache + slot * row_vecs;
+    u32x4 *vd = v_cache + slot * row_vecs;
+    for (int c = threadIdx.x; c < row_vecs; c += blockDim.x) {
+      const u32x4 kv = ks[c], vv = vs[c];
+      kd[c] = kv;
+      vd[c] = vv;
+    }
+  }
+}
+
+// grid = (pairs, chunks of one block, 2 tensors).  Each workgroup copies up to
+// 256 threads x 4 vectors = 16 KiB of one block of one tensor.
+constexpr int kCopyVecsPerThread = 4;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyChunk = kCopyThreads * kCopyVecsPerThread;
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(u32x4 *__restrict__ k_cache,
+                                                                   u32x4 *__restrict__ v_cache,
+                                                                   const int64_t *__restrict__ pairs,
+                                                                   int64_t block_vecs, int32_t num_blocks) {
+  const int64_t pair = blockIdx.x;
+  const int64_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;  // skipped pair
+  u32x4 *pool = blockIdx.z == 0 ? k_cache : v_cache;
+  const u32x4 *s = pool + src * block_vecs;
+  u32x4 *d = pool + dst * block_vecs;
+  const int64_t c0 = (int64_t)blockIdx.y * kCopyChunk + threadIdx.x;
+  u32x4 buf[kCopyVecsPerThread];
+#pragma unroll
+  for (int i = 0; i < kCopyVecsPerThread; ++i) {
+    const int64_t c = c0 + (int64_t)i * kCopyThreads;
+    if (c < block_vecs) buf[i] = s[c];
+  }
+#pragma unroll
+  for (int i = 0; i < kCopyVecsPerThread; ++i) {
+    const int64_t c = c0 + (int64_t)i * kCopyThreads;
+    if (c < block_vecs) d[c] = buf[i];
+  }
+}
+
+static bool shape_ok(int32_t block_size, int32_t num_kv_heads, int32_t head_dim) {
+  return (head_dim == 64 || head_dim == 128) &&
+         (block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32) && num_kv_heads >= 1;
+}
+
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                     const int64_t *slot_mapping, int64_t num_tokens, int32_t num_blocks,
+                                     int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                                     void *stream) {
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (!shape_ok(block_size, num_kv_heads, head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t elem = dtype == PKV_DTYPE_F32 ? 4 : 2;
+  const int row_vecs = (int)((int64_t)num_kv_heads * head_dim * elem / 16);
+  const int threads = row_vecs >= 256 ? 256 : (row_vecs >= 128 ? 128 : 64);
+  const unsigned grid = (unsigned)(num_tokens < (1 << 20) ? num_tokens : (1 << 20));
+  hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream,
+                     (const u32x4 *)k_new, (const u32x4 *)v_new, (u32x4 *)k_cache, (u32x4 *)v_cache, slot_mapping,
+                     num_tokens, row_vecs, (int64_t)num_blocks * block_size);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mapping, int64_t num_pairs,
+                                  int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                  pkv_dtype dtype, void *stream) {
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (!shape_ok(block_size, num_kv_heads, head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PKV_OK;
+  if (num_pairs > 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  if (!k_cache || !v_cache || !block_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_mapping, 8)) return PKV_ERR_INVALID_ARG;
+  const int64_t elem = dtype == PKV_DTYPE_F32 ? 4 : 2;
+  const int64_t block_vecs = (int64_t)block_size * num_kv_heads * head_dim * elem / 16;
+  const int64_t chunks = (block_vecs + kCopyChunk - 1) / kCopyChunk;
+  if (chunks > 65535) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)chunks, 2), dim3(kCopyThreads), 0,
+                     (hipStream_t)stream, (u32x4 *)k_cache, (u32x4 *)v_cache, block_mapping, block_vecs, num_blocks);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" const char *pkv_status_string(pkv_status status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
