@@ -71,13 +71,16 @@ def measured_traffic(workload: str, per_launch_alg: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int):
+def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered"):
     import torch
     from paged_kv_cache_148_amd import batch, binding
 
     cfg = workloads.CONFIGS[name]
     t_gen = time.time()
     wl = workloads.make_workload(cfg)
+    if layout == "contiguous":
+        # identity free stack: every sequence's blocks are consecutive and ascending
+        wl.free_order = list(range(wl.num_blocks))
     step = batch.step_for(wl, which)
     bf16 = cfg.dtype == "bf16"
     dev = "cuda"
@@ -123,7 +126,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int):
     attn_s = float(np.mean(attn_ms)) / 1e3
     nb = algorithmic_bytes(cfg, step)
     res = {
-        "workload": name, "step": which, "partition_size": partition,
+        "workload": name, "step": which, "partition_size": partition, "layout": layout,
         "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
         "attention_us_p10": attn_ms[len(attn_ms) // 10] * 1e3, "attention_us_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
         "step_gbs": nb["step"] / step_s / 1e9,
@@ -192,6 +195,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous"],
+                    help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -204,7 +209,7 @@ def main():
 
     main_part = PARTITION[args.workload] if args.partition is None else args.partition
     which = "steady"
-    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part)
+    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout)
     print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step, attention {res['attention_us_mean']:.1f} us, "
           f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)

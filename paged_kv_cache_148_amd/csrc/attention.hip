@@ -23,8 +23,8 @@
 //     each lane's V operand is one 16-byte row piece of 4 tokens, regrouped in
 //     registers (no LDS round trip for V).
 //   attn_vec_kernel   (everything else: g = 1, fp32, D = 64, small blocks): one token
-//     row per D*e/16 lanes, 16-byte loads along head_dim, q.k by packed bf16 dot
-//     products or fp32 FMAs, row sums by DPP.
+//     row per D*e/16 lanes, 16-byte loads along head_dim, q.k as fp32 FMAs on exactly
+//     widened elements, row sums by DPP.
 // Scores carry scale * log2(e) so every exponential is a hardware exp2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,6 +56,24 @@ struct AttnArgs {
   int max_parts;
   float scale_log2;  // scale * log2(e)
 };
+
+// Work-item order across the chip.  Workgroups go round-robin to the 8 XCDs by their
+// 1-D index.  The logical order has the KV head fastest (then partition, then sequence),
+// so with Hkv a multiple of 8 each XCD receives the same KV heads of every (sequence,
+// partition) -- identical amounts of work -- whatever the context-length mix.  (With the
+// partition index fastest, XCD x would receive only partitions p = x mod 8, and short
+// contexts would leave half the XCDs idle.)
+struct WorkItem {
+  int p, kvh, s;
+};
+__device__ __forceinline__ WorkItem work_item(int Hkv, int parts) {
+  const int w = (int)blockIdx.x;
+  WorkItem it;
+  it.kvh = w % Hkv;
+  it.p = (w / Hkv) % parts;
+  it.s = w / (Hkv * parts);
+  return it;
+}
 
 // Merge weight of a partial state with max m into a combined max M (empty state -> 0).
 __device__ __forceinline__ float merge_weight(float m, float M) { return m == kNegInf ? 0.f : fast_exp2(m - M); }
@@ -133,7 +151,8 @@ template <int B>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int D = 128;
   constexpr int OS = D + 4;   // padded head stride in LDS
-  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const WorkItem wi = work_item(a.Hkv, a.max_parts);
+  const int p = wi.p, kvh = wi.kvh, s = wi.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, grp = lane >> 4;
   const int g = a.g;
@@ -177,23 +196,43 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   const uint32_t k_off = (uint32_t)(c16 * tok_stride + 8 * grp);
   const uint32_t v_off = (uint32_t)(4 * grp * tok_stride + 8 * c16);
 
-  const int tile_hi = (t1 + 15) >> 4;
-  for (int tile = (t0 >> 4) + wave; tile < tile_hi; tile += kWaves) {
-    const int tok0 = tile << 4;
-    int phys = __builtin_amdgcn_readfirstlane(table[tok0 / B]);
+  // This wave's tiles are tile_lo + wave + kWaves * i, i = 0 .. n_my - 1.  Their block-table
+  // entries are fetched 64 at a time (one per lane) and read back with readlane, and the
+  // K/V loads of tile i + 1 are issued before tile i is computed.
+  const int tile_lo = t0 >> 4, tile_hi = (t1 + 15) >> 4;
+  const int n_my = tile_hi - tile_lo > wave ? (tile_hi - tile_lo - wave + kWaves - 1) / kWaves : 0;
+  auto table_chunk = [&](int i0) -> int {
+    const int i = i0 + lane;
+    return i < n_my ? table[((tile_lo + wave + kWaves * i) << 4) / B] : 0;
+  };
+  int tb = 0;
+  auto issue = [&](int i, u32x4 *kd, u32x4 *vd) {
+    int phys = __builtin_amdgcn_readlane(tb, i & 63);
     if ((unsigned)phys >= (unsigned)a.N) {
       bad = 1;
       phys = 0;
     }
+    const int tok0 = (tile_lo + wave + kWaves * i) << 4;
     const size_t base = ((size_t)phys * B + (tok0 % B)) * tok_stride;
     const uint16_t *kb = kpool + base + k_off;
     const uint16_t *vb = vpool + base + v_off;
-    u32x4 kr[4], vr[4];
+    // K: each instruction covers 64 bytes of a row, so consecutive instructions share a
+    // 128-byte line -- ordinary loads keep it cached for the second half.  V: whole rows
+    // per instruction, streamed past the caches.
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kr[c] = ld16(kb + 32 * c);
+    for (int c = 0; c < 4; ++c) kd[c] = ld16(kb + 32 * c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = ld16(vb + r * tok_stride);
+    for (int r = 0; r < 4; ++r) vd[r] = ld16_stream(vb + r * tok_stride);
+  };
 
+  // Tiles are computed in pairs from two register buffers; while one tile is computed the
+  // loads of the next are in flight.  Every issue is unconditional (past the chunk's last
+  // tile it re-reads that tile, which the caches still hold), so the count of loads in
+  // flight is the same on every path and each wait covers only the tile about to be used.
+  // An odd tile count leaves a phantom second tile whose positions are all masked.
+  auto compute = [&](int i, u32x4 *kr, u32x4 *vr, bool real) {
+    const int tok0 = (tile_lo + wave + kWaves * i) << 4;
+    const int lim = real ? t1 : 0;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -203,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     float sv[4], mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = tok0 + 4 * grp + r < t1;
+      const bool ok = tok0 + 4 * grp + r < lim;
       sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
       if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
       mx = fmaxf(mx, sv[r]);
@@ -221,17 +260,17 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     lsum = lsum * alpha + ps;
     if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
     }
     m = mnew;
 
     const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
     const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int w = i >> 1;
+    for (int j = 0; j < 8; ++j) {
+      const int w = j >> 1;
       uint32_t a01, a23;
-      if (i & 1) {
+      if (j & 1) {
         a01 = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
         a23 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
       } else {
@@ -239,7 +278,22 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         a23 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
       }
       const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[i], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[j], 0, 0, 0);
+    }
+  };
+
+  for (int c0 = 0; c0 < n_my; c0 += 64) {
+    tb = table_chunk(c0);
+    const int cn = min(64, n_my - c0);
+    u32x4 ka[4], va[4], kb[4], vb[4];
+    issue(c0, ka, va);
+    for (int ii = 0; ii < cn; ii += 2) {
+      issue(c0 + min(ii + 1, cn - 1), kb, vb);
+      __builtin_amdgcn_sched_barrier(0);   // keep the next tile's loads ahead of this wait
+      compute(c0 + ii, ka, va, true);
+      issue(c0 + min(ii + 2, cn - 1), ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c0 + ii + 1, kb, vb, ii + 1 < cn);
     }
   }
 
@@ -278,7 +332,8 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
   constexpr int STEPS = CH / TPW;
   constexpr int OS = D + 4;
   constexpr bool kBF16 = sizeof(T) == 2;
-  const int p = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+  const WorkItem wi = work_item(a.Hkv, a.max_parts);
+  const int p = wi.p, kvh = wi.kvh, s = wi.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane / LPT, cl = lane % LPT;
   const int g = a.g;
@@ -320,32 +375,54 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
   const T *kpool = reinterpret_cast<const T *>(a.k) + (size_t)kvh * D + cl * EPL;
   const T *vpool = reinterpret_cast<const T *>(a.v) + (size_t)kvh * D + cl * EPL;
 
-  const int u_hi = (t1 + CH - 1) / CH;
-  for (int u = t0 / CH + wave; u < u_hi; u += kWaves) {
-    const int tokc = u * CH;
-    u32x4 kr[STEPS], vr[STEPS];
-    bool ok[STEPS];
+  // This wave's units are u_lo + wave + kWaves * i, i = 0 .. n_my - 1.  With one block per
+  // unit its table entries are fetched 64 at a time (one per lane) and read back with
+  // readlane; the K/V loads of unit i + 1 are issued before unit i is computed.
+  const int u_lo = t0 / CH, u_hi = (t1 + CH - 1) / CH;
+  const int n_my = u_hi - u_lo > wave ? (u_hi - u_lo - wave + kWaves - 1) / kWaves : 0;
+  auto table_chunk = [&](int i0) -> int {
+    const int i = i0 + lane;
+    return i < n_my ? table[u_lo + wave + kWaves * i] : 0;
+  };
+  int tb = 0;
+  auto issue = [&](int i, u32x4 *kd, u32x4 *vd, bool *okd) {
+    const int tokc = (u_lo + wave + kWaves * i) * CH;
+    int uphys = 0;
+    if constexpr (B >= TPW) {
+      uphys = __builtin_amdgcn_readlane(tb, i & 63);
+      if ((unsigned)uphys >= (unsigned)a.N) {
+        bad = 1;
+        uphys = 0;
+      }
+    }
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       const int t = tokc + st * TPW + row;
-      ok[st] = t >= t0 && t < t1;
-      int phys = 0;
-      if constexpr (B >= TPW) {
-        // the unit is one block and starts inside [t0, t1): its table entry is in use
-        phys = __builtin_amdgcn_readfirstlane(table[tokc / B]);
-      } else {
+      okd[st] = t >= t0 && t < t1;
+      int phys = uphys;
+      if constexpr (B < TPW) {
         // the unit spans several blocks: only positions in [t0, t1) consult the table
-        if (ok[st]) phys = table[t / B];
-      }
-      if ((unsigned)phys >= (unsigned)a.N) {
-        bad = 1;
-        phys = 0;
+        phys = okd[st] ? table[t / B] : 0;
+        if ((unsigned)phys >= (unsigned)a.N) {
+          bad = 1;
+          phys = 0;
+        }
       }
       const size_t off = ((size_t)phys * B + (t % B)) * tok_stride;
-      kr[st] = ld16(kpool + off);
-      vr[st] = ld16(vpool + off);
-      if (!ok[st]) vr[st] = (u32x4){0u, 0u, 0u, 0u};
+      kd[st] = ld16_stream(kpool + off);
+      vd[st] = ld16_stream(vpool + off);
     }
+  };
+
+  // Same pipeline as the MFMA kernel: units in pairs from two register buffers, every
+  // issue unconditional, a phantom (fully masked) second unit for odd counts.
+  auto compute = [&](u32x4 *kr, u32x4 *vr, const bool *ok_in, bool real) {
+    bool ok[STEPS];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) ok[st] = ok_in[st] && real;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st)
+      if (!ok[st]) vr[st] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       if (j >= g) break;
@@ -356,9 +433,10 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
         float part = 0.f;
         if constexpr (kBF16) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kr[st][w]),
-                                                   __builtin_bit_cast(bf16x2, qraw[j][w]), part, false);
+          for (int w = 0; w < 4; ++w) {
+            part = fmaf(bf16_lo(kr[st][w]), bf16_lo(qraw[j][w]), part);
+            part = fmaf(bf16_hi(kr[st][w]), bf16_hi(qraw[j][w]), part);
+          }
         } else {
 #pragma unroll
           for (int w = 0; w < 4; ++w) part = fmaf(__uint_as_float(kr[st][w]), __uint_as_float(qraw[j][w]), part);
@@ -392,6 +470,22 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
         }
       }
       m[j] = mnew;
+    }
+  };
+
+  for (int c0 = 0; c0 < n_my; c0 += 64) {
+    if constexpr (B >= TPW) tb = table_chunk(c0);
+    const int cn = min(64, n_my - c0);
+    u32x4 ka[STEPS], va[STEPS], kb[STEPS], vb[STEPS];
+    bool oka[STEPS], okb[STEPS];
+    issue(c0, ka, va, oka);
+    for (int ii = 0; ii < cn; ii += 2) {
+      issue(c0 + min(ii + 1, cn - 1), kb, vb, okb);
+      __builtin_amdgcn_sched_barrier(0);   // keep the next unit's loads ahead of this wait
+      compute(ka, va, oka, true);
+      issue(c0 + min(ii + 2, cn - 1), ka, va, oka);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kb, vb, okb, ii + 1 < cn);
     }
   }
 
@@ -605,7 +699,9 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   a.scale_log2 = scale * kLog2e;
 
   hipStream_t st = (hipStream_t)stream;
-  const dim3 grid((unsigned)np, (unsigned)num_kv_heads, (unsigned)num_seqs);
+  const int64_t items = np * num_kv_heads * (int64_t)num_seqs;
+  if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)items);
   const bool bf16 = dtype == PKV_DTYPE_BF16;
   if (path == PKV_PATH_MFMA) {
     if (block_size == 16)

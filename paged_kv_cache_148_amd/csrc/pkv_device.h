@@ -17,6 +17,11 @@ constexpr float kNegInf = -__builtin_inff();
 // 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// 16-byte load with the non-temporal hint, for data read exactly once (the K/V stream):
+// it keeps the caches for data with reuse and streams markedly faster on gfx950.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // bf16 is the high half of an fp32 word: widening is a shift (low element) or a mask
 // (high element) of a packed pair.
