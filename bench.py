@@ -150,6 +150,25 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     return res, wl, step
 
 
+def copy_probe(reps: int = 3) -> None:
+    """copy_blocks over a known byte count, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE:
+    16384 blocks of 32 KiB copied in each of K and V = 1 GiB read + 1 GiB written per call."""
+    import torch
+    from paged_kv_cache_148_amd import binding
+    N, B, Hkv, D = 32768, 16, 8, 128
+    kc = torch.zeros(N, B, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    half = N // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half, N)], dim=1).to(torch.int64).cuda()
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        binding.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    nbytes = 2 * half * B * Hkv * D * 2
+    print(json.dumps({"copy_probe": True, "calls": reps, "bytes_read_per_call": nbytes,
+                      "bytes_written_per_call": nbytes}), flush=True)
+
+
 def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
     """The CPU oracle on the same inputs: whole-step passes (copies, write, attention) on all
     host cores, repeated until about budget_s seconds have been spent."""
@@ -195,6 +214,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
     ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous"],
                     help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool")
     args = ap.parse_args()
@@ -206,6 +227,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     main_part = PARTITION[args.workload] if args.partition is None else args.partition
     which = "steady"
