@@ -96,7 +96,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     out = torch.empty_like(q)
     ws_bytes = binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim, step.max_context_len,
                                                 partition)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)   # queue counters start at zero
     torch.cuda.synchronize()
     gen_s = time.time() - t_gen
     n_pairs = step.copy_pairs.shape[0]

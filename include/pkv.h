@@ -73,9 +73,10 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, v
                           void *stream);
 
 /*
- * pkv_attention_workspace_size -- bytes of fp32 scratch that paged_attention_decode
- * needs for its split-context partials, given the host-side maximum context length.
- * 0 when partition_size == 0 or when no sequence can span more than one partition.
+ * pkv_attention_workspace_size -- bytes of device scratch that paged_attention_decode
+ * needs: a 256-byte work-queue header, followed, when a sequence can span more than one
+ * partition, by the fp32 partial states of the split (given the host-side maximum context
+ * length).  Always at least 256.
  */
 size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                     int32_t max_context_len, int32_t partition_size);
@@ -101,9 +102,15 @@ pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, int32_t hea
  *
  * partition_size == 0: each (sequence, KV head) is one unit of work.  Otherwise
  * (a multiple of block_size; a multiple of 16 on the MFMA path) the context is cut
- * into partitions of that many tokens, partial softmax states go to `workspace`
- * (at least pkv_attention_workspace_size bytes, 16-byte aligned) and a second kernel
- * merges them by log-sum-exp in a fixed order, so results are deterministic.
+ * into partitions of that many tokens, partial softmax states go to the workspace and
+ * a second kernel merges them by log-sum-exp in a fixed order, so results are
+ * deterministic.
+ *
+ * workspace: caller-owned device memory of at least pkv_attention_workspace_size bytes,
+ * 16-byte aligned, always required.  Its first 256 bytes are the work-queue counters of
+ * the persistent kernels: they must be zero before the first call that uses the
+ * workspace (clear them once when it is allocated) and every call leaves them zero.
+ * Calls that share a workspace must not overlap (issue them on one stream).
  * max_context_len must bound every context_lens[s] and fit the table
  * (max_context_len <= max_blocks_per_seq * block_size); a sequence may span at most
  * 8192 partitions (PKV_ERR_UNSUPPORTED beyond).

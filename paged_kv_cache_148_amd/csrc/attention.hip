@@ -8,12 +8,21 @@
 // PidokuInfra topic 10, section 5 "The kernel side"); the result is the ordinary
 // attention over the gathered rows (page "PagedAttention", tokentrails, step 3).
 //
-// Work unit: one workgroup (4 waves) per (context partition, KV head, sequence).  It
-// serves every query head of the KV head's group, so each K/V byte is read once per
-// group.  Without a partition size the partition is the whole context.  With one,
-// each workgroup leaves a partial state (running max m, sum l, unnormalised o) in the
-// workspace and attn_reduce_kernel merges the partials by log-sum-exp.  Sequences
-// whose context fits one partition are finished in pass 1.
+// Work unit: one (KV head, context partition, sequence) item, processed by one
+// workgroup of 4 waves.  An item serves every query head of the KV head's group, so each
+// K/V byte is read once per group.  Without a partition size the partition is the whole
+// context.  With one, an item leaves a partial state (running max m, sum l, unnormalised
+// o) in the workspace and attn_reduce_kernel merges the partials by log-sum-exp;
+// sequences whose context fits one partition are finished in pass 1.
+//
+// Scheduling: the pass-1 kernels are persistent.  As many workgroups as fit on the chip
+// each build, in LDS, the prefix sum of per-sequence item counts from context_lens (so
+// only non-empty items exist).  Workgroup b starts with item b and then takes items in
+// order from a work-queue counter in the workspace until none are left; the kernel that
+// follows (the merge, or a one-thread reset) returns the counter to zero.  A dynamic
+// queue keeps every XCD busy until the end even though the XCDs do not run at identical
+// speeds, and no launch slot is spent on empty partitions.  Batches too large to stage in
+// LDS fall back to one workgroup per possible item.
 //
 // Two pass-1 kernels:
 //   attn_mfma_kernel  (bf16, D = 128, B % 16 == 0, 2 <= g <= 16): a 16-token tile of
@@ -37,7 +46,10 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMfmaDepth = 3;          // tiles in flight per wave on the MFMA path
 constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
+constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (2 x 16 KiB)
+constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the workspace
 
 struct AttnArgs {
   void *out;
@@ -55,6 +67,9 @@ struct AttnArgs {
   int P;             // partition length in tokens (whole context when not splitting)
   int max_parts;
   float scale_log2;  // scale * log2(e)
+  int S;             // sequences
+  unsigned *queue;   // [0]: items taken beyond the grid (zero between calls)
+  int persistent;    // 1: persistent workgroups + work queue; 0: one workgroup per possible item
 };
 
 // Work-item order across the chip.  Workgroups go round-robin to the 8 XCDs by their
@@ -73,6 +88,86 @@ __device__ __forceinline__ WorkItem work_item(int Hkv, int parts) {
   it.p = (w / Hkv) % parts;
   it.s = w / (Hkv * parts);
   return it;
+}
+
+// Work-queue schedule.  Item counts per sequence: ceil(ctx / P) partitions times Hkv
+// (one item per KV head for a sequence with an unusable length, which only writes its
+// fill value).  sm_pref receives the inclusive prefix sum and sm_ctx the lengths; the
+// return value is the total number of items.
+__device__ int build_schedule(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_tmp) {
+  const int S = a.S, tid = threadIdx.x;
+  const int per = (S + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, S), hi = min(lo + per, S);
+  int run = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int c = a.ctx[i];
+    sm_ctx[i] = c;
+    const int np = (c >= 1 && c <= a.max_ctx) ? (c + a.P - 1) / a.P : 1;
+    run += np * a.Hkv;
+    sm_pref[i] = run;
+  }
+  int x = run;   // inclusive scan of the per-thread runs: within the wave, then across waves
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if ((tid & 63) >= off) x += y;
+  }
+  if ((tid & 63) == 63) sm_tmp[tid >> 6] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < (tid >> 6); ++w) before += sm_tmp[w];
+  const int excl = before + x - run;
+  for (int i = lo; i < hi; ++i) sm_pref[i] += excl;
+  __syncthreads();
+  return sm_pref[S - 1];
+}
+
+// Item w -> (sequence, partition, KV head): the first sequence whose inclusive prefix
+// exceeds w, then KV head fastest within it.
+__device__ __forceinline__ WorkItem decode_item(int w, const int *sm_pref, int S, int Hkv) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (sm_pref[mid] > w) hi = mid; else lo = mid + 1;
+  }
+  const int r = w - (lo ? sm_pref[lo - 1] : 0);
+  WorkItem it;
+  it.s = lo;
+  it.kvh = r % Hkv;
+  it.p = r / Hkv;
+  return it;
+}
+
+// Common driver of the pass-1 kernels: persistent work-queue loop, or one item per
+// workgroup.  ITEM(s, p, kvh, ctx) processes an item (ctx < 0: read it from memory).
+struct SchedSmem {
+  int tmp[kWaves];
+  int next;
+};
+template <typename Item>
+__device__ __forceinline__ void run_items(const AttnArgs &a, SchedSmem &sc, int *sm_dyn, Item item) {
+  if (!a.persistent) {
+    const WorkItem it = work_item(a.Hkv, a.max_parts);
+    item(it.s, it.p, it.kvh, -1);
+    return;
+  }
+  const int tid = threadIdx.x;
+  int *sm_pref = sm_dyn, *sm_ctx = sm_dyn + a.S;
+  const int total = build_schedule(a, sm_pref, sm_ctx, sc.tmp);
+  // Workgroup b starts with item b; later items come one at a time from the queue counter,
+  // which counts items beyond the grid.  The next index is fetched while the current item
+  // runs.
+  int w = (int)blockIdx.x;
+  while (w < total) {
+    unsigned c = 0;
+    if (tid == 0) c = atomicAdd(&a.queue[0], 1u);
+    const WorkItem it = decode_item(w, sm_pref, a.S, a.Hkv);
+    item(it.s, it.p, it.kvh, sm_ctx[it.s]);
+    if (tid == 0) sc.next = (int)(gridDim.x + c);
+    __syncthreads();
+    w = sc.next;
+    __syncthreads();
+  }
 }
 
 // Merge weight of a partial state with max m into a combined max M (empty state -> 0).
@@ -146,22 +241,51 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
 //       d = 8*c16 .. 8*c16+7 of tokens 4grp + r: one 16-byte load per token, regrouped
 //       into (token pair, d) halves with byte permutes.  The accumulator of MFMA i holds,
 //       in lane l, row 4grp + r' -> d = 32*grp + 8*r' + i of head c16.
+//
+// Loads are buffer loads through a per-tile descriptor held in SGPRs (base = the tile's
+// first row, range = the tile's 16 rows), so the lane offsets are loop invariant.  A
+// tile past the end gets a zero-range descriptor: its loads return zeros without a
+// memory access, which keeps the number of loads in flight the same on every path.
 // ---------------------------------------------------------------------------
-template <int B>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
+constexpr int kBufferConfig = 0x00020000;   // buffer descriptor word 3 for gfx9-family parts
+constexpr int kNontemporal = 2;             // buffer load cache-policy bit: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)bytes, kBufferConfig);
+}
+
+constexpr int kMfmaOS = 128 + 4;   // padded head stride of the LDS merge buffer
+struct MfmaSmem {
+  float o[kWaves][16][kMfmaOS];
+  float m[kWaves][16], l[kWaves][16];
+  int bad[kWaves];
+};
+
+template <int B, int NBUF>
+__device__ __forceinline__ void mfma_item(const AttnArgs &a, int s, int p, int kvh, int ctx_known, MfmaSmem &sm) {
   constexpr int D = 128;
-  constexpr int OS = D + 4;   // padded head stride in LDS
-  const WorkItem wi = work_item(a.Hkv, a.max_parts);
-  const int p = wi.p, kvh = wi.kvh, s = wi.s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int OS = kMfmaOS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile addresses in SGPRs
   const int c16 = lane & 15, grp = lane >> 4;
   const int g = a.g;
+  float (*sm_o)[16][OS] = sm.o;
+  float (*sm_m)[16] = sm.m;
+  float (*sm_l)[16] = sm.l;
+  int *sm_bad = sm.bad;
 
-  __shared__ float sm_o[kWaves][16][OS];
-  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
-  __shared__ int sm_bad[kWaves];
-
-  const int ctx = a.ctx[s];
+  // This wave's tiles are tile_lo + wave + kWaves * i.  Their block-table entries are
+  // fetched 64 at a time (one per lane; the first batch together with the context length,
+  // bounded by the table row rather than the context) and read back with readlane.
+  const int32_t *table = a.tables + (size_t)s * a.max_blocks;
+  const int tile_lo = (p * a.P) >> 4;
+  auto table_chunk = [&](int i0) -> int {
+    const int tok = (tile_lo + wave + kWaves * (i0 + lane)) << 4;
+    const int e = tok / B;
+    return e < a.max_blocks ? table[e] : 0;
+  };
+  int tb = table_chunk(0);
+  const int ctx = ctx_known >= 0 ? ctx_known : a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx) {
     if (p == 0) fill_group<uint16_t, D>(a, s, kvh * g, g, ctx < 1 ? 0.f : __builtin_nanf(""));
     return;
@@ -170,6 +294,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   if (t0 >= ctx) return;
   const int t1 = min(t0 + a.P, ctx);
   const bool single = ctx <= a.P;
+  const int tile_hi = (t1 + 15) >> 4;
+  const int n_my = tile_hi - tile_lo > wave ? (tile_hi - tile_lo - wave + kWaves - 1) / kWaves : 0;
 
   // Q^T operand: head c16 of the group (zero columns past g).
   bf16x8 qop[4];
@@ -189,50 +315,37 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   int bad = 0;
 
-  const int32_t *table = a.tables + (size_t)s * a.max_blocks;
-  const size_t tok_stride = (size_t)a.Hkv * D;   // elements between consecutive slots
-  const uint16_t *kpool = reinterpret_cast<const uint16_t *>(a.k) + (size_t)kvh * D;
-  const uint16_t *vpool = reinterpret_cast<const uint16_t *>(a.v) + (size_t)kvh * D;
-  const uint32_t k_off = (uint32_t)(c16 * tok_stride + 8 * grp);
-  const uint32_t v_off = (uint32_t)(4 * grp * tok_stride + 8 * c16);
+  const uint32_t tsb = (uint32_t)a.Hkv * D * 2;           // bytes between consecutive slots
+  const uint32_t tile_bytes = 16 * tsb;
+  const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)kvh * D * 2;
+  const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)kvh * D * 2;
+  const uint32_t k_voff = c16 * tsb + 16 * grp;           // token c16, bytes 64c + 16grp
+  const uint32_t v_voff = 4 * grp * tsb + 16 * c16;       // tokens 4grp + r, bytes 16 c16
 
-  // This wave's tiles are tile_lo + wave + kWaves * i, i = 0 .. n_my - 1.  Their block-table
-  // entries are fetched 64 at a time (one per lane) and read back with readlane, and the
-  // K/V loads of tile i + 1 are issued before tile i is computed.
-  const int tile_lo = t0 >> 4, tile_hi = (t1 + 15) >> 4;
-  const int n_my = tile_hi - tile_lo > wave ? (tile_hi - tile_lo - wave + kWaves - 1) / kWaves : 0;
-  auto table_chunk = [&](int i0) -> int {
-    const int i = i0 + lane;
-    return i < n_my ? table[((tile_lo + wave + kWaves * i) << 4) / B] : 0;
-  };
-  int tb = 0;
-  auto issue = [&](int i, u32x4 *kd, u32x4 *vd) {
+  // issue the loads of chunk-local tile i (a zero-range descriptor past the chunk)
+  auto issue = [&](int c0, int i, int cn, u32x4 *kd, u32x4 *vd) {
+    const bool live = i < cn;
     int phys = __builtin_amdgcn_readlane(tb, i & 63);
-    if ((unsigned)phys >= (unsigned)a.N) {
+    if (live && (unsigned)phys >= (unsigned)a.N) {
       bad = 1;
       phys = 0;
     }
-    const int tok0 = (tile_lo + wave + kWaves * i) << 4;
-    const size_t base = ((size_t)phys * B + (tok0 % B)) * tok_stride;
-    const uint16_t *kb = kpool + base + k_off;
-    const uint16_t *vb = vpool + base + v_off;
-    // K: each instruction covers 64 bytes of a row, so consecutive instructions share a
-    // 128-byte line -- ordinary loads keep it cached for the second half.  V: whole rows
-    // per instruction, streamed past the caches.
+    const int tok0 = (tile_lo + wave + kWaves * (c0 + i)) << 4;
+    const size_t off = ((size_t)phys * B + (tok0 % B)) * tsb;
+    const uint32_t range = live ? tile_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + off, range);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + off, range);
+    // K: each instruction covers 64 bytes of a row and consecutive instructions share a
+    // 128-byte line, so K keeps the default cache policy; V rows are whole per instruction
+    // and are streamed (non-temporal).
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kd[c] = ld16(kb + 32 * c);
+    for (int c = 0; c < 4; ++c) kd[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, 64 * c, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vd[r] = ld16_stream(vb + r * tok_stride);
+    for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff, r * tsb, kNontemporal);
   };
 
-  // Tiles are computed in pairs from two register buffers; while one tile is computed the
-  // loads of the next are in flight.  Every issue is unconditional (past the chunk's last
-  // tile it re-reads that tile, which the caches still hold), so the count of loads in
-  // flight is the same on every path and each wait covers only the tile about to be used.
-  // An odd tile count leaves a phantom second tile whose positions are all masked.
-  auto compute = [&](int i, u32x4 *kr, u32x4 *vr, bool real) {
+  auto compute = [&](int i, u32x4 *kr, u32x4 *vr) {
     const int tok0 = (tile_lo + wave + kWaves * i) << 4;
-    const int lim = real ? t1 : 0;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -242,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     float sv[4], mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = tok0 + 4 * grp + r < lim;
+      const bool ok = tok0 + 4 * grp + r < t1;
       sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
       if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
       mx = fmaxf(mx, sv[r]);
@@ -282,18 +395,24 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     }
   };
 
+  // NBUF-deep ring of register buffers.  Pipeline step k issues tile k into buffer k % NBUF
+  // and computes tile k - (NBUF - 1); the loop is unrolled by NBUF so buffer indices are
+  // compile-time constants and every load sits inside the loop.  Issues past the chunk are
+  // zero-range (no memory access), computes outside [0, cn) are skipped by a wave-uniform
+  // branch, so the count of loads in flight is fixed and each wait covers one tile.
   for (int c0 = 0; c0 < n_my; c0 += 64) {
-    tb = table_chunk(c0);
+    if (c0 > 0) tb = table_chunk(c0);
     const int cn = min(64, n_my - c0);
-    u32x4 ka[4], va[4], kb[4], vb[4];
-    issue(c0, ka, va);
-    for (int ii = 0; ii < cn; ii += 2) {
-      issue(c0 + min(ii + 1, cn - 1), kb, vb);
-      __builtin_amdgcn_sched_barrier(0);   // keep the next tile's loads ahead of this wait
-      compute(c0 + ii, ka, va, true);
-      issue(c0 + min(ii + 2, cn - 1), ka, va);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(c0 + ii + 1, kb, vb, ii + 1 < cn);
+    u32x4 kbuf[NBUF][4], vbuf[NBUF][4];
+    for (int k0 = 0; k0 < cn + NBUF - 1; k0 += NBUF) {
+#pragma unroll
+      for (int j = 0; j < NBUF; ++j) {
+        const int k = k0 + j;
+        issue(c0, k, cn, kbuf[j], vbuf[j]);
+        __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
+        const int kc = k - (NBUF - 1);
+        if (kc >= 0 && kc < cn) compute(c0 + kc, kbuf[(j + 1) % NBUF], vbuf[(j + 1) % NBUF]);
+      }
     }
   }
 
@@ -316,6 +435,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   finish_group<uint16_t, D, 16, OS>(a, s, kvh, p, single, sm_m, sm_l, sm_o, sm_bad);
 }
 
+template <int B, int NBUF>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
+  __shared__ MfmaSmem sm;
+  __shared__ SchedSmem sc;
+  extern __shared__ int sm_dyn[];
+  run_items(a, sc, sm_dyn, [&](int s, int p, int kvh, int ctx) { mfma_item<B, NBUF>(a, s, p, kvh, ctx, sm); });
+}
+
 // ---------------------------------------------------------------------------
 // Vector path.  T = float or uint16_t (bf16).  Each token row of a KV head is
 // D*sizeof(T) bytes = LPT lanes x 16 bytes; a wave covers TPW = 64 / LPT rows at once.
@@ -323,8 +450,15 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 // Every row keeps its own online-softmax state; rows and waves are merged at the end.
 // The wave's unit of work is CH = max(B, TPW) consecutive tokens (STEPS row steps).
 // ---------------------------------------------------------------------------
+template <int G, int D>
+struct VecSmem {
+  float o[kWaves][G][D + 4];
+  float m[kWaves][G], l[kWaves][G];
+  int bad[kWaves];
+};
+
 template <typename T, int D, int G, int B>
-__global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
+__device__ __forceinline__ void vec_item(const AttnArgs &a, int s, int p, int kvh, int ctx_known, VecSmem<G, D> &sm) {
   constexpr int EPL = 16 / (int)sizeof(T);
   constexpr int LPT = D / EPL;
   constexpr int TPW = 64 / LPT;
@@ -332,17 +466,16 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
   constexpr int STEPS = CH / TPW;
   constexpr int OS = D + 4;
   constexpr bool kBF16 = sizeof(T) == 2;
-  const WorkItem wi = work_item(a.Hkv, a.max_parts);
-  const int p = wi.p, kvh = wi.kvh, s = wi.s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile addresses in SGPRs
   const int row = lane / LPT, cl = lane % LPT;
   const int g = a.g;
+  float (*sm_o)[G][OS] = sm.o;
+  float (*sm_m)[G] = sm.m;
+  float (*sm_l)[G] = sm.l;
+  int *sm_bad = sm.bad;
 
-  __shared__ float sm_o[kWaves][G][OS];
-  __shared__ float sm_m[kWaves][G], sm_l[kWaves][G];
-  __shared__ int sm_bad[kWaves];
-
-  const int ctx = a.ctx[s];
+  const int ctx = ctx_known >= 0 ? ctx_known : a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx) {
     if (p == 0) fill_group<T, D>(a, s, kvh * g, g, ctx < 1 ? 0.f : __builtin_nanf(""));
     return;
@@ -523,6 +656,14 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
   finish_group<T, D, G, OS>(a, s, kvh, p, single, sm_m, sm_l, sm_o, sm_bad);
 }
 
+template <typename T, int D, int G, int B>
+__global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
+  __shared__ VecSmem<G, D> sm;
+  __shared__ SchedSmem sc;
+  extern __shared__ int sm_dyn[];
+  run_items(a, sc, sm_dyn, [&](int s, int p, int kvh, int ctx) { vec_item<T, D, G, B>(a, s, p, kvh, ctx, sm); });
+}
+
 // ---------------------------------------------------------------------------
 // Pass 2: merge the partials of one (sequence, head):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p l_p.
@@ -552,6 +693,7 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
   __shared__ f32x4 sm_acc[kThreads];
   __shared__ float red[kWaves];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  if (h == 0 && s == 0 && tid == 0) a.queue[0] = 0u;   // pass 1 is complete: reset its work queue
   const int ctx = a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
   const int np = (ctx + a.P - 1) / a.P;
@@ -584,6 +726,11 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
   }
 }
 
+// Queue reset when no merge kernel follows pass 1.
+__global__ void queue_reset_kernel(unsigned *queue) {
+  if (threadIdx.x == 0) queue[0] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -599,24 +746,43 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   return vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
 }
 
+typedef void (*Pass1Fn)(AttnArgs);
+
 template <typename T, int D, int G>
-static void launch_vec_b(dim3 grid, hipStream_t st, const AttnArgs &a, int B) {
+static Pass1Fn vec_fn_b(int B) {
   switch (B) {
-    case 4: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 4>), grid, dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 8>), grid, dim3(kThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 16>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((attn_vec_kernel<T, D, G, 32>), grid, dim3(kThreads), 0, st, a); break;
+    case 4: return attn_vec_kernel<T, D, G, 4>;
+    case 8: return attn_vec_kernel<T, D, G, 8>;
+    case 16: return attn_vec_kernel<T, D, G, 16>;
+    default: return attn_vec_kernel<T, D, G, 32>;
   }
 }
 
 template <typename T, int D>
-static void launch_vec(dim3 grid, hipStream_t st, const AttnArgs &a, int B) {
-  switch (vec_group(a.g)) {
-    case 1: launch_vec_b<T, D, 1>(grid, st, a, B); break;
-    case 2: launch_vec_b<T, D, 2>(grid, st, a, B); break;
-    case 4: launch_vec_b<T, D, 4>(grid, st, a, B); break;
-    default: launch_vec_b<T, D, 8>(grid, st, a, B); break;
+static Pass1Fn vec_fn(int g, int B) {
+  switch (vec_group(g)) {
+    case 1: return vec_fn_b<T, D, 1>(B);
+    case 2: return vec_fn_b<T, D, 2>(B);
+    case 4: return vec_fn_b<T, D, 4>(B);
+    default: return vec_fn_b<T, D, 8>(B);
   }
+}
+
+static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g) {
+  if (path == PKV_PATH_MFMA) return B == 16 ? attn_mfma_kernel<16, kMfmaDepth> : attn_mfma_kernel<32, kMfmaDepth>;
+  if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
+  return D == 128 ? vec_fn<float, 128>(g, B) : vec_fn<float, 64>(g, B);
+}
+
+// Workgroups of `fn` that fit on the current device at once.
+static int resident_workgroups(Pass1Fn fn, size_t dyn_lds) {
+  int dev = 0, cus = 0, occ = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(fn), kThreads, dyn_lds) !=
+      hipSuccess)
+    return 0;
+  return (occ > 0 ? occ : 1) * cus;
 }
 
 template <typename T, int D>
@@ -639,10 +805,11 @@ extern "C" pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, 
 
 extern "C" size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                int32_t max_context_len, int32_t partition_size) {
-  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  if (partition_size <= 0 || num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    return kQueueBytes;
   const int64_t np = parts_for(max_context_len, partition_size);
-  if (np <= 1) return 0;
-  return (size_t)num_seqs * num_heads * np * (head_dim + 2) * sizeof(float);
+  if (np <= 1) return kQueueBytes;
+  return kQueueBytes + (size_t)num_seqs * num_heads * np * (head_dim + 2) * sizeof(float);
 }
 
 extern "C" pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -671,11 +838,9 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
 
   const int64_t P = partition_size > 0 ? partition_size : ((int64_t)max_context_len + 15) / 16 * 16;
   const int64_t np = parts_for(max_context_len, P);
-  if (np > 1) {
-    if (np > kMaxReduceParts) return PKV_ERR_UNSUPPORTED;
-    const size_t need = pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
-  }
+  if (np > kMaxReduceParts) return PKV_ERR_UNSUPPORTED;
+  const size_t need = pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
 
   AttnArgs a;
   a.out = out;
@@ -685,7 +850,8 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   a.tables = block_tables;
   a.ctx = context_lens;
   const size_t nparts_total = (size_t)num_seqs * num_heads * (size_t)np;
-  a.ws_o = np > 1 ? reinterpret_cast<float *>(workspace) : nullptr;
+  a.queue = reinterpret_cast<unsigned *>(workspace);
+  a.ws_o = np > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kQueueBytes) : nullptr;
   a.ws_m = np > 1 ? a.ws_o + nparts_total * head_dim : nullptr;
   a.ws_l = np > 1 ? a.ws_m + nparts_total : nullptr;
   a.max_blocks = max_blocks_per_seq;
@@ -697,25 +863,36 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   a.P = (int)P;
   a.max_parts = (int)np;
   a.scale_log2 = scale * kLog2e;
+  a.S = num_seqs;
 
   hipStream_t st = (hipStream_t)stream;
-  const int64_t items = np * num_kv_heads * (int64_t)num_seqs;
+  const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
-  const dim3 grid((unsigned)items);
   const bool bf16 = dtype == PKV_DTYPE_BF16;
-  if (path == PKV_PATH_MFMA) {
-    if (block_size == 16)
-      hipLaunchKernelGGL((attn_mfma_kernel<16>), grid, dim3(kThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_mfma_kernel<32>), grid, dim3(kThreads), 0, st, a);
-  } else if (bf16) {
-    if (head_dim == 128) launch_vec<uint16_t, 128>(grid, st, a, block_size);
-    else launch_vec<uint16_t, 64>(grid, st, a, block_size);
-  } else {
-    if (head_dim == 128) launch_vec<float, 128>(grid, st, a, block_size);
-    else launch_vec<float, 64>(grid, st, a, block_size);
+  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g);
+  // persistent workgroups when the schedule fits in LDS, else one workgroup per possible item
+  size_t dyn_lds = 0;
+  int64_t grid = items;
+  a.persistent = 0;
+  if (num_seqs <= kMaxSchedSeqs) {
+    dyn_lds = 2 * (size_t)num_seqs * sizeof(int);
+    const int resident = resident_workgroups(fn, dyn_lds);
+    if (resident > 0) {
+      a.persistent = 1;
+      grid = items < resident ? items : resident;
+    } else {
+      dyn_lds = 0;
+    }
   }
+  void *args[] = {&a};
+  if (hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid), dim3(kThreads), args, dyn_lds, st) !=
+      hipSuccess)
+    return PKV_ERR_HIP;
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  if (np <= 1 && a.persistent) {
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, a.queue);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
   if (np > 1) {
     const dim3 rgrid((unsigned)num_heads, (unsigned)num_seqs);
     if (bf16) {

@@ -43,11 +43,11 @@ def test_status_strings(L):
 
 
 def test_workspace_size(L):
-    # S * Hq * ceil(max_ctx / P) * (D + 2) fp32
-    assert binding.attention_workspace_size(8, 32, 128, 131072, 512) == 8 * 32 * 256 * 130 * 4
-    assert binding.attention_workspace_size(8, 32, 128, 100, 512) == 0      # one partition
-    assert binding.attention_workspace_size(8, 32, 128, 1000, 0) == 0       # no split
-    assert binding.attention_workspace_size(2, 4, 64, 513, 512) == 2 * 4 * 2 * 66 * 4
+    # 256-byte work-queue header + S * Hq * ceil(max_ctx / P) * (D + 2) fp32 partials when split
+    assert binding.attention_workspace_size(8, 32, 128, 131072, 512) == 256 + 8 * 32 * 256 * 130 * 4
+    assert binding.attention_workspace_size(8, 32, 128, 100, 512) == 256    # one partition
+    assert binding.attention_workspace_size(8, 32, 128, 1000, 0) == 256     # no split
+    assert binding.attention_workspace_size(2, 4, 64, 513, 512) == 256 + 2 * 4 * 2 * 66 * 4
 
 
 def test_path_selection(L):
@@ -110,6 +110,9 @@ def test_attention_host_checks(L):
     assert _attn(L, maxctx=0) == PKV_ERR_INVALID_ARG
     assert _attn(L, P=24) == PKV_ERR_INVALID_ARG                     # not a multiple of B
     assert _attn(L, P=32) == PKV_ERR_INVALID_ARG                     # needs a workspace
+    assert _attn(L, P=0) == PKV_ERR_INVALID_ARG                      # the queue header is always needed
+    assert _attn(L, P=0, ws=FAKE, wsb=255) == PKV_ERR_INVALID_ARG
+    assert _attn(L, P=0, ws=ODD, wsb=256) == PKV_ERR_INVALID_ARG
     need = binding.attention_workspace_size(4, 8, 128, 128, 32)
     assert _attn(L, P=32, ws=FAKE, wsb=need - 4) == PKV_ERR_INVALID_ARG
     assert _attn(L, scale=float("nan")) == PKV_ERR_INVALID_ARG

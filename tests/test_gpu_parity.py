@@ -347,3 +347,47 @@ def test_bad_device_values_give_defined_outputs():
     assert (o[0] == 0).all()
     assert np.isnan(o[1]).all() and np.isnan(o[2]).all()
     assert H.bits(out)[3].tobytes() == good[3].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# scheduling: persistent work queue and the large-batch fallback
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,P", [("gqa70b", 512), ("mha7b", 0), ("tiny_fp32", 8)])
+def test_work_queue_counters_return_to_zero(name, P):
+    import torch
+    wl = _wl(name, num_seqs=min(12, workloads.CONFIGS[name].num_seqs))
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P, do_attn=False)          # the step's copies and write, as the oracle does
+    cfg = wl.cfg
+    ws = torch.zeros(binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim,
+                                                      step.max_context_len, P), dtype=torch.uint8, device="cuda")
+    first = None
+    for _ in range(3):
+        binding.paged_attention_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                       d["context_lens"], step.max_context_len, wl.scale, P, ws)
+        torch.cuda.synchronize()
+        assert not ws[:8].any().item(), "work-queue counters must be zero after a call"
+        got = H.bits(d["out"]).copy()
+        if first is None:
+            first = got
+        assert got.tobytes() == first.tobytes()
+    _, _, _, ref = H.oracle_step(wl, "steady", P)
+    H.check_close(first, ref, cfg.dtype, f"queue {name}")
+
+
+def test_large_batch_uses_fallback_grid():
+    # more sequences than the persistent schedule stages in LDS: one workgroup per item
+    cfg = workloads.Config("many", "bf16", 4500, 8, 2, 128, 16, ("uniform", 1, 40), seed=77)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    rng = np.random.default_rng(1)
+    items = np.unique(rng.integers(0, cfg.num_seqs * cfg.num_heads, size=200))
+    for P in (0, 16):
+        _say("fallback grid", cfg.num_seqs, "P", P)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P)
+        _, _, _, ref = H.oracle_step(wl, "steady", P, items=items)
+        got = H.bits(d["out"]).reshape(cfg.num_seqs * cfg.num_heads, -1)[items]
+        H.check_close(got, ref, "bf16", f"fallback P={P}")
