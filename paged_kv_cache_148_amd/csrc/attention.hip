@@ -232,9 +232,10 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
 //
 // Lane l of a wave: c16 = l % 16, grp = l / 16.
 //   QK  (v_mfma_f32_16x16x32_bf16, A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]):
-//       lane l loads token c16's d-slice 32c + 8grp .. +7 for c = 0..3 and the same
-//       slice of head c16's q row.  Result S^T: lane l holds tokens 4grp + r (r = 0..3)
-//       of head c16.
+//       lane l needs token c16's d-slice 32c + 8grp .. +7 for c = 0..3 and the same
+//       slice of head c16's q row.  K is loaded as whole rows (like V, below) and turned
+//       into this layout through a per-wave LDS staging tile.  Result S^T: lane l holds
+//       tokens 4grp + r (r = 0..3) of head c16.
 //   P.V (v_mfma_f32_16x16x16_bf16, A = V^T [16 d-rows x 16 tokens], B = P^T [16 tokens x
 //       16 heads]): B is exactly the S^T result layout (head c16, tokens 4grp + r).  MFMA
 //       number i (0..7) gives A-row c16 the head-dim index 8*c16 + i, so lane l needs
@@ -259,6 +260,7 @@ struct MfmaSmem {
   float o[kWaves][16][kMfmaOS];
   float m[kWaves][16], l[kWaves][16];
   int bad[kWaves];
+  u32x4 kst[kWaves][256];   // per-wave staging of one K tile (16 tokens x 16 chunks of 16 B)
 };
 
 template <int B, int NBUF>
@@ -319,8 +321,8 @@ __device__ __forceinline__ void mfma_item(const AttnArgs &a, int s, int p, int k
   const uint32_t tile_bytes = 16 * tsb;
   const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)kvh * D * 2;
   const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)kvh * D * 2;
-  const uint32_t k_voff = c16 * tsb + 16 * grp;           // token c16, bytes 64c + 16grp
-  const uint32_t v_voff = 4 * grp * tsb + 16 * c16;       // tokens 4grp + r, bytes 16 c16
+  const uint32_t row_voff = 4 * grp * tsb + 16 * c16;     // tokens 4grp + r, bytes 16 c16 (whole rows)
+  u32x4 *kst = sm.kst[wave];
 
   // issue the loads of chunk-local tile i (a zero-range descriptor past the chunk)
   auto issue = [&](int c0, int i, int cn, u32x4 *kd, u32x4 *vd) {
@@ -335,21 +337,32 @@ __device__ __forceinline__ void mfma_item(const AttnArgs &a, int s, int p, int k
     const uint32_t range = live ? tile_bytes : 0u;
     const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + off, range);
     const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + off, range);
-    // K: each instruction covers 64 bytes of a row and consecutive instructions share a
-    // 128-byte line, so K keeps the default cache policy; V rows are whole per instruction
-    // and are streamed (non-temporal).
+    // K and V alike: instruction r reads whole 256-byte rows (tokens 4grp + r, 16 lanes
+    // per row), streamed past the caches (non-temporal).
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kd[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, 64 * c, 0);
+    for (int r = 0; r < 4; ++r) kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, row_voff, r * tsb, kNontemporal);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, v_voff, r * tsb, kNontemporal);
+    for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, row_voff, r * tsb, kNontemporal);
   };
 
   auto compute = [&](int i, u32x4 *kr, u32x4 *vr) {
     const int tok0 = (tile_lo + wave + kWaves * i) << 4;
+    // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t sits at
+    // t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token, 16 chunks)
+    // and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of 64 banks.
+    // Lane (c16, grp) then holds token c16, chunks 4c + grp = head dims 32c + 8grp .. +7.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * grp + r;
+      kst[t * 16 + (c16 ^ t)] = kr[r];
+    }
+    u32x4 kop[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[c]), qop[c], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]), qop[c], sc, 0, 0, 0);
 
     // scores of tokens tok0 + 4grp + r for head c16; positions past the end are masked
     float sv[4], mx = kNegInf;
