@@ -76,7 +76,9 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, v
  * pkv_attention_workspace_size -- bytes of device scratch that paged_attention_decode
  * needs: a 256-byte work-queue header, followed, when a sequence can span more than one
  * partition, by the fp32 partial states of the split (given the host-side maximum context
- * length).  Always at least 256.
+ * length): num_seqs * num_heads * partitions * (head_dim + 32) floats -- the unnormalised
+ * partial outputs, then one 128-byte line of (max, sum) pairs per (sequence, KV head,
+ * partition), sized as if every head had its own KV head.  Always at least 256.
  */
 size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                     int32_t max_context_len, int32_t partition_size);
@@ -113,7 +115,8 @@ pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, int32_t hea
  * Calls that share a workspace must not overlap (issue them on one stream).
  * max_context_len must bound every context_lens[s] and fit the table
  * (max_context_len <= max_blocks_per_seq * block_size); a sequence may span at most
- * 8192 partitions (PKV_ERR_UNSUPPORTED beyond).
+ * 8192 partitions, max_context_len at most 2^30 and max_blocks_per_seq at most 2^29
+ * (PKV_ERR_UNSUPPORTED beyond).
  *
  * Device values: context_lens[s] <= 0 gives out[s] = 0; context_lens[s] >
  * max_context_len, or a table entry read that lies outside [0, num_blocks), gives

@@ -24,8 +24,12 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of the device code: the compiler only
-# emits ordinary fp32 instructions.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# emits ordinary fp32 instructions.  The atomic optimizer is off: it would turn the
+# single-lane work-queue fetch into a wave-wide reduction whose result is consumed at
+# once, which waits for every load in flight (the attention kernels keep tiles in flight
+# across that fetch).
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function", "-munsafe-fp-atomics"]
 

@@ -18,20 +18,20 @@
 // Scheduling: the pass-1 kernels are persistent.  As many workgroups as fit on the chip
 // each build, in LDS, the prefix sum of per-sequence item counts from context_lens (so
 // only non-empty items exist).  Workgroup b starts with item b and then takes items in
-// order from a work-queue counter in the workspace until none are left; the kernel that
-// follows (the merge, or a one-thread reset) returns the counter to zero.  A dynamic
+// order from a work-queue counter in the workspace until none are left; the last
+// workgroup to finish returns the counters to zero.  A dynamic
 // queue keeps every XCD busy until the end even though the XCDs do not run at identical
 // speeds, and no launch slot is spent on empty partitions.  Batches too large to stage in
 // LDS fall back to one workgroup per possible item.
 //
 // Two pass-1 kernels:
-//   attn_mfma_kernel  (bf16, D = 128, B % 16 == 0, 2 <= g <= 16): a 16-token tile of
+//   attn_mfma_kernel  (bf16, D = 128, B in {16, 32}, 1 <= g <= 16): a 16-token tile of
 //     K times the group's Q^T on v_mfma_f32_16x16x32_bf16 gives the score tile; the
 //     probabilities stay in the MFMA result layout and feed v_mfma_f32_16x16x16_bf16
 //     against V^T for P.V.  The head dimension of the P.V product is permuted so that
 //     each lane's V operand is one 16-byte row piece of 4 tokens, regrouped in
 //     registers (no LDS round trip for V).
-//   attn_vec_kernel   (everything else: g = 1, fp32, D = 64, small blocks): one token
+//   attn_vec_kernel   (everything else: fp32, D = 64, small blocks): one token
 //     row per D*e/16 lanes, 16-byte loads along head_dim, q.k as fp32 FMAs on exactly
 //     widened elements, row sums by DPP.
 // Scores carry scale * log2(e) so every exponential is a hardware exp2.
@@ -46,9 +46,10 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMfmaDepth = 3;          // tiles in flight per wave on the MFMA path
+constexpr int kMfmaDepth = 4;          // MFMA path: tiles per wave in the load ring (NB - 1 ahead)
 constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
-constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (2 x 16 KiB)
+constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
+constexpr int kClasses = 16;            // length classes of the longest-first schedule
 constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the workspace
 
 struct AttnArgs {
@@ -58,9 +59,9 @@ struct AttnArgs {
   const void *v;
   const int32_t *tables;
   const int32_t *ctx;
-  float *ws_o;       // [S, Hq, max_parts, D]
-  float *ws_m;       // [S, Hq, max_parts]   log2-domain running max
-  float *ws_l;       // [S, Hq, max_parts]
+  float *ws_o;       // [S, Hq, max_parts, D]  unnormalised partial outputs
+  float *ws_ml;      // [S, Hkv, max_parts, 32]: (m, l) of query head j of the group at 2j, 2j+1;
+                     // m in the log2 domain.  One 128-byte line per item, written whole.
   int max_blocks;    // table row length
   int max_ctx;       // host bound on ctx
   int Hq, Hkv, g, N;
@@ -138,7 +139,17 @@ __device__ __forceinline__ WorkItem decode_item(int w, const int *sm_pref, int S
   return it;
 }
 
-// Common driver of the pass-1 kernels: persistent work-queue loop, or one item per
+// End of a persistent launch for one workgroup: the last one to finish returns the queue
+// counters to zero for the next call.  Every workgroup's fetches from queue[0] have
+// returned before it counts itself done in queue[1], so the reset follows all of them.
+__device__ __forceinline__ void queue_done(unsigned *queue) {
+  if (threadIdx.x == 0 && atomicAdd(&queue[1], 1u) == gridDim.x - 1) {
+    atomicExch(&queue[0], 0u);
+    atomicExch(&queue[1], 0u);
+  }
+}
+
+// Common driver of the vector pass-1 kernel: persistent work-queue loop, or one item per
 // workgroup.  ITEM(s, p, kvh, ctx) processes an item (ctx < 0: read it from memory).
 struct SchedSmem {
   int tmp[kWaves];
@@ -168,6 +179,7 @@ __device__ __forceinline__ void run_items(const AttnArgs &a, SchedSmem &sc, int 
     w = sc.next;
     __syncthreads();
   }
+  queue_done(a.queue);
 }
 
 // Merge weight of a partial state with max m into a combined max M (empty state -> 0).
@@ -220,15 +232,16 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
       const size_t part = ((size_t)s * a.Hq + h) * a.max_parts + p;
       a.ws_o[part * D + d] = o;
       if (d == 0) {
-        a.ws_m[part] = M;
-        a.ws_l[part] = L;
+        float *ml = a.ws_ml + (((size_t)s * a.Hkv + kvh) * a.max_parts + p) * 32;
+        ml[2 * j] = M;
+        ml[2 * j + 1] = L;
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: bf16, D = 128, B in {16, 32}, group of up to 16 query heads.
+// MFMA path: bf16, D = 128, B in {16, 32}, a group of 1 to 16 query heads.
 //
 // Lane l of a wave: c16 = l % 16, grp = l / 16.
 //   QK  (v_mfma_f32_16x16x32_bf16, A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]):
@@ -243,219 +256,558 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
 //       into (token pair, d) halves with byte permutes.  The accumulator of MFMA i holds,
 //       in lane l, row 4grp + r' -> d = 32*grp + 8*r' + i of head c16.
 //
-// Loads are buffer loads through a per-tile descriptor held in SGPRs (base = the tile's
-// first row, range = the tile's 16 rows), so the lane offsets are loop invariant.  A
-// tile past the end gets a zero-range descriptor: its loads return zeros without a
-// memory access, which keeps the number of loads in flight the same on every path.
+// Streaming.  Each wave sees one flat stream of 16-token tiles: the tiles of its share of
+// the current item, then those of the next item.  Loads run NB - 1 tiles ahead of the
+// compute, across the item boundary, so the first tiles of the next item are already in
+// flight while the current item's states are merged.  The next item's block-table entries
+// and q slice are loaded into registers one item ahead.  Every item's loop is padded to a
+// multiple of NB tiles (at least NB); padded and out-of-range tiles get a zero-range
+// buffer descriptor, so their loads return zeros without a memory access and every path
+// through the loop issues the same loads -- the compiler's wait counts then stay exact.
 // ---------------------------------------------------------------------------
 constexpr int kBufferConfig = 0x00020000;   // buffer descriptor word 3 for gfx9-family parts
 constexpr int kNontemporal = 2;             // buffer load cache-policy bit: non-temporal
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)bytes, kBufferConfig);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferConfig);
 }
 
 constexpr int kMfmaOS = 128 + 4;   // padded head stride of the LDS merge buffer
 struct MfmaSmem {
-  float o[kWaves][16][kMfmaOS];
-  float m[kWaves][16], l[kWaves][16];
-  int bad[kWaves];
+  // per-wave states of the item being merged; two sets, alternating between items, so one
+  // barrier per item separates the writes of an item from the reads of the one before
+  float o[2][kWaves][16][kMfmaOS];
+  alignas(16) float m[2][16][kWaves];   // [head][wave]: one 16-byte read per head
+  alignas(16) float l[2][16][kWaves];
+  int bad[2][kWaves];
   u32x4 kst[kWaves][256];   // per-wave staging of one K tile (16 tokens x 16 chunks of 16 B)
+  int red[kWaves * (kClasses + 1)];   // schedule scan
+  int nextw[2];             // item indices taken from the queue, two items ahead
 };
 
-template <int B, int NBUF>
-__device__ __forceinline__ void mfma_item(const AttnArgs &a, int s, int p, int kvh, int ctx_known, MfmaSmem &sm) {
+// One work item as a wave sees it.  Every field is wave-uniform.
+struct MItem {
+  int s, p, kvh;
+  int t1;        // end of the attended token range (exclusive)
+  int tile_lo;   // first 16-token tile of the partition
+  int n_my;      // this wave's live tiles: tile_lo + wave + kWaves * i, i < n_my
+  int n_pad;     // loop length: n_my rounded up to a multiple of NB, at least NB
+  int fill;      // 0 attend; 1 write zeros; 2 write NaN; 3 nothing to do
+  int single;    // the partition is the whole context: normalise into out
+};
+
+// Longest-first schedule of the MFMA kernel.  The queue hands out, first, every full
+// partition (P tokens) of every sequence in sequence order, then the last -- or only --
+// partition of each sequence, longest first: the lengths fall into kClasses classes of
+// equal width and a stable counting sort orders the sequences by class.  The longest
+// items start first and the last ones to finish are short, so the workgroups run out of
+// work together.  Every workgroup builds the same order from context_lens.
+// LDS (dynamic): pref[S] (inclusive prefix of full-partition items), ctx[S], order[S].
+struct LptSched {
+  int total_full;   // items of the full partitions
+  int total;        // all items
+};
+
+__device__ __forceinline__ int length_class(int len, int lmax) {
+  return kClasses - 1 - min(kClasses - 1, (int)(((long long)len * kClasses) / ((long long)lmax + 1)));
+}
+
+__device__ LptSched build_lpt_schedule(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order, int *sm_red) {
+  const int S = a.S, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (S + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, S), hi = min(lo + per, S);
+  const int lmax = min(a.P, a.max_ctx);   // the longest possible last partition
+  constexpr int NV = kClasses + 1;        // scanned values: full-partition items, then class counts
+  int v[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int c = a.ctx[i];
+    sm_ctx[i] = c;
+    const bool ok = c >= 1 && c <= a.max_ctx;
+    const int np = ok ? (c + a.P - 1) / a.P : 1;
+    v[0] += (np - 1) * a.Hkv;
+    sm_pref[i] = v[0];
+    const int cls = length_class(ok ? c - (np - 1) * a.P : 0, lmax);
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) v[1 + k] += cls == k;
+  }
+  // exclusive prefix of every value over the threads: inclusive scan in the wave, then the
+  // wave totals through LDS
+  int x[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) x[k] = v[k];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int y = __shfl_up(x[k], off);
+      if (lane >= off) x[k] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) sm_red[wv * NV + k] = x[k];
+  }
+  __syncthreads();
+  int base[NV], tot[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    int before = 0, all = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = sm_red[w * NV + k];
+      before += w < wv ? t : 0;
+      all += t;
+    }
+    base[k] = before + x[k] - v[k];   // this thread's exclusive prefix
+    tot[k] = all;
+  }
+  // class k's sequences start after all those of the longer classes
+  int cstart = 0;
+#pragma unroll
+  for (int k = 0; k < kClasses; ++k) {
+    base[1 + k] += cstart;
+    cstart += tot[1 + k];
+  }
+  for (int i = lo; i < hi; ++i) {
+    sm_pref[i] += base[0];
+    const int c = sm_ctx[i];
+    const bool ok = c >= 1 && c <= a.max_ctx;
+    const int np = ok ? (c + a.P - 1) / a.P : 1;
+    const int cls = length_class(ok ? c - (np - 1) * a.P : 0, lmax);
+    int pos = 0;
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) {
+      if (cls == k) {
+        pos = base[1 + k];
+        base[1 + k] += 1;
+      }
+    }
+    sm_order[pos] = i;
+  }
+  __syncthreads();
+  LptSched r;
+  r.total_full = tot[0];
+  r.total = tot[0] + S * a.Hkv;
+  return r;
+}
+
+// Item w of the longest-first order -> (sequence, partition, KV head), KV head fastest.
+__device__ __forceinline__ WorkItem decode_lpt(int w, const LptSched &sc, const int *sm_pref, const int *sm_ctx,
+                                               const int *sm_order, const AttnArgs &a) {
+  WorkItem it;
+  if (w < sc.total_full) {
+    int lo = 0, hi = a.S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sm_pref[mid] > w) hi = mid; else lo = mid + 1;
+    }
+    const int r = w - (lo ? sm_pref[lo - 1] : 0);
+    it.s = lo;
+    it.kvh = r % a.Hkv;
+    it.p = r / a.Hkv;
+  } else {
+    const int r = w - sc.total_full;
+    it.s = min(max(sm_order[r / a.Hkv], 0), a.S - 1);   // in range whatever LDS holds
+    it.kvh = r % a.Hkv;
+    const int c = sm_ctx[it.s];
+    it.p = (c >= 1 && c <= a.max_ctx) ? (c - 1) / a.P : 0;
+  }
+  return it;
+}
+
+template <int NB>
+__device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int kvh, int ctx, int wave) {
+  MItem it;
+  it.s = s;
+  it.p = p;
+  it.kvh = kvh;
+  it.tile_lo = (p * a.P) >> 4;
+  it.t1 = 0;
+  it.n_my = 0;
+  it.single = 0;
+  if (ctx < 1 || ctx > a.max_ctx) {
+    it.fill = p == 0 ? (ctx < 1 ? 1 : 2) : 3;
+  } else if (p * a.P >= ctx) {
+    it.fill = 3;
+  } else {
+    it.fill = 0;
+    it.t1 = min(p * a.P + a.P, ctx);
+    it.single = ctx <= a.P;
+    const int nt = ((it.t1 + 15) >> 4) - it.tile_lo;
+    it.n_my = nt > wave ? (nt - wave + kWaves - 1) / kWaves : 0;
+  }
+  it.n_pad = max(NB, (it.n_my + NB - 1) / NB * NB);
+  return it;
+}
+
+// An empty item: what the stream holds past the workgroup's last item.
+__device__ __forceinline__ MItem no_item() {
+  MItem it;
+  it.s = it.p = it.kvh = it.t1 = it.tile_lo = it.n_my = it.single = 0;
+  it.n_pad = 0;
+  it.fill = 3;
+  return it;
+}
+
+// Block-table entries of tiles 64c .. 64c + 63 of an item, one per lane (zero past the
+// table row or for an item with nothing to attend).
+template <int B>
+__device__ __forceinline__ int table_chunk(const AttnArgs &a, const MItem &it, int c, int wave, int lane) {
+  const bool live = it.fill == 0 && 64 * c < it.n_my;
+  const __amdgpu_buffer_rsrc_t r =
+      buf_rsrc(a.tables + (size_t)it.s * a.max_blocks, live ? (uint32_t)a.max_blocks * 4u : 0u);
+  const int tok = (it.tile_lo + wave + kWaves * (64 * c + lane)) << 4;
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (tok / B) * 4, 0, 0);
+}
+
+// The Q^T operand of an item: head c16 of the KV head's group (zero columns past g).
+__device__ __forceinline__ void load_q(const AttnArgs &a, const MItem &it, int c16, int grp, u32x4 *qd) {
+  constexpr int D = 128;
+  const bool live = it.fill == 0;
+  const __amdgpu_buffer_rsrc_t r =
+      buf_rsrc(reinterpret_cast<const uint16_t *>(a.q) + ((size_t)it.s * a.Hq + (size_t)it.kvh * a.g) * D,
+               live ? (uint32_t)(a.g * D * 2) : 0u);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qd[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
+}
+
+// Item index -> item.  Persistent launch: from the LDS schedule; otherwise one item per
+// workgroup in the fixed grid order, with the length read from memory.
+// Item fields come from LDS and memory (vector registers); they are the same in every lane.
+__device__ __forceinline__ MItem uniform(MItem it) {
+  it.s = __builtin_amdgcn_readfirstlane(it.s);
+  it.p = __builtin_amdgcn_readfirstlane(it.p);
+  it.kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
+  it.tile_lo = __builtin_amdgcn_readfirstlane(it.tile_lo);
+  it.n_my = __builtin_amdgcn_readfirstlane(it.n_my);
+  it.n_pad = __builtin_amdgcn_readfirstlane(it.n_pad);
+  it.fill = __builtin_amdgcn_readfirstlane(it.fill);
+  it.single = __builtin_amdgcn_readfirstlane(it.single);
+  return it;
+}
+
+template <int NB>
+__device__ __forceinline__ MItem item_at(const AttnArgs &a, int w, const LptSched &sc, const int *sm_pref,
+                                         const int *sm_ctx, const int *sm_order, int wave) {
+  const int total = sc.total;
+  if (w >= total) return no_item();
+  if (a.persistent) {
+    const WorkItem wi = decode_lpt(w, sc, sm_pref, sm_ctx, sm_order, a);
+    return uniform(make_item<NB>(a, wi.s, wi.p, wi.kvh, sm_ctx[wi.s], wave));
+  }
+  const int kvh = w % a.Hkv, p = (w / a.Hkv) % a.max_parts, s = w / (a.Hkv * a.max_parts);
+  return uniform(make_item<NB>(a, s, p, kvh, a.ctx[s], wave));
+}
+
+// Merge of the four waves' states of an item, then its output (normalised, or a partial
+// state for the second pass).  Thread t covers head t / 16 of the group and head dims
+// 8 (t % 16) .. +7: ten independent LDS reads and one wait, then 16-byte stores.
+__device__ __forceinline__ void mfma_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
+                                            const float (*sm_l)[kWaves], const float (*sm_o)[16][kMfmaOS],
+                                            const int *sm_bad) {
+  constexpr int D = 128;
+  const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 8;
+  const bool act = j < a.g;   // heads past the group: their (unwritten) LDS rows are read, not used
+  const f32x4 m4 = *reinterpret_cast<const f32x4 *>(sm_m[j]);
+  const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sm_l[j]);
+  f32x4 olo[kWaves], ohi[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    olo[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d0]);
+    ohi[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d0 + 4]);
+  }
+  const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m4[w]);
+  float L = 0.f;
+  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float wt = merge_weight(m4[w], M);
+    L += wt * l4[w];
+    lo += wt * olo[w];
+    hi += wt * ohi[w];
+  }
+  if (bad) {
+    M = 0.f;
+    L = __builtin_nanf("");
+    lo = hi = (f32x4){L, L, L, L};
+  }
+  const int h = it.kvh * a.g + j;
+  if (it.single) {
+    if (act) {
+      u32x4 v;
+      v[0] = pack_bf16x2(lo[0] / L, lo[1] / L);
+      v[1] = pack_bf16x2(lo[2] / L, lo[3] / L);
+      v[2] = pack_bf16x2(hi[0] / L, hi[1] / L);
+      v[3] = pack_bf16x2(hi[2] / L, hi[3] / L);
+      st16(reinterpret_cast<uint16_t *>(a.out) + ((size_t)it.s * a.Hq + h) * D + d0, v);
+    }
+  } else {
+    if (act) {
+      const size_t part = ((size_t)it.s * a.Hq + h) * a.max_parts + it.p;
+      *reinterpret_cast<f32x4 *>(a.ws_o + part * D + d0) = lo;
+      *reinterpret_cast<f32x4 *>(a.ws_o + part * D + d0 + 4) = hi;
+    }
+    // (m, l) of the group's heads fill the item's whole 128-byte line (zeros past the
+    // group): lanes 0, 32, .. write heads j and j + 1, so no line is shared between items
+    const float M1 = __shfl_down(M, 16), L1 = __shfl_down(L, 16);   // head j + 1 is lane t + 16
+    if ((t & 31) == 0) {
+      const bool act1 = j + 1 < a.g;
+      const f32x4 v = {act ? M : 0.f, act ? L : 0.f, act1 ? M1 : 0.f, act1 ? L1 : 0.f};
+      const size_t item = ((size_t)it.s * a.Hkv + it.kvh) * a.max_parts + it.p;
+      *reinterpret_cast<f32x4 *>(a.ws_ml + item * 32 + 2 * j) = v;
+    }
+  }
+}
+
+template <int B, int NB>
+__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int D = 128;
   constexpr int OS = kMfmaOS;
+  __shared__ MfmaSmem sm;
+  extern __shared__ int sm_dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile addresses in SGPRs
   const int c16 = lane & 15, grp = lane >> 4;
-  const int g = a.g;
-  float (*sm_o)[16][OS] = sm.o;
-  float (*sm_m)[16] = sm.m;
-  float (*sm_l)[16] = sm.l;
-  int *sm_bad = sm.bad;
+  int *sm_pref = sm_dyn, *sm_ctx = sm_dyn + a.S, *sm_order = sm_dyn + 2 * a.S;
 
-  // This wave's tiles are tile_lo + wave + kWaves * i.  Their block-table entries are
-  // fetched 64 at a time (one per lane; the first batch together with the context length,
-  // bounded by the table row rather than the context) and read back with readlane.
-  const int32_t *table = a.tables + (size_t)s * a.max_blocks;
-  const int tile_lo = (p * a.P) >> 4;
-  auto table_chunk = [&](int i0) -> int {
-    const int tok = (tile_lo + wave + kWaves * (i0 + lane)) << 4;
-    const int e = tok / B;
-    return e < a.max_blocks ? table[e] : 0;
-  };
-  int tb = table_chunk(0);
-  const int ctx = ctx_known >= 0 ? ctx_known : a.ctx[s];
-  if (ctx < 1 || ctx > a.max_ctx) {
-    if (p == 0) fill_group<uint16_t, D>(a, s, kvh * g, g, ctx < 1 ? 0.f : __builtin_nanf(""));
-    return;
+  // The workgroup's items: it_0 = blockIdx.x, then one index per queue fetch.  The fetch
+  // for it_{k+2} is made while it_k runs, so both the current and the next item are
+  // always known.
+  LptSched sched;
+  if (a.persistent) {
+    if (tid == 0) sm.nextw[1] = (int)(gridDim.x + atomicAdd(&a.queue[0], 1u));
+    sched = build_lpt_schedule(a, sm_pref, sm_ctx, sm_order, sm.red);   // ends with a barrier
+  } else {
+    sched.total_full = 0;
+    sched.total = (int)gridDim.x;
   }
-  const int t0 = p * a.P;
-  if (t0 >= ctx) return;
-  const int t1 = min(t0 + a.P, ctx);
-  const bool single = ctx <= a.P;
-  const int tile_hi = (t1 + 15) >> 4;
-  const int n_my = tile_hi - tile_lo > wave ? (tile_hi - tile_lo - wave + kWaves - 1) / kWaves : 0;
+  const int total = sched.total;
+  int w = (int)blockIdx.x;
+  int wn = a.persistent ? sm.nextw[1] : total;
+  if (w < total) {
+    MItem cur = item_at<NB>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
+    MItem nxt;
 
-  // Q^T operand: head c16 of the group (zero columns past g).
-  bf16x8 qop[4];
-  {
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + ((size_t)s * a.Hq + kvh * g + c16) * D;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (c16 < g) v = ld16(qrow + 32 * c + 8 * grp);
-      qop[c] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
+    const uint32_t tsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive slots
+    const uint32_t tile_bytes = 16 * tsb;
+    const char *kpool = reinterpret_cast<const char *>(a.k);
+    const char *vpool = reinterpret_cast<const char *>(a.v);
+    const uint32_t row_voff = 4 * grp * tsb + 16 * c16;   // tokens 4grp + r, bytes 16 c16 (whole rows)
+    u32x4 *kst = sm.kst[wave];
 
-  float m = kNegInf, lsum = 0.f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  int bad = 0;
+    // registers of the stream: table chunks (current item: the chunk being issued and the
+    // one after it; next item: its first two), q operands, validity flags
+    int tb_cur = table_chunk<B>(a, cur, 0, wave, lane);
+    int tb_ahead = table_chunk<B>(a, cur, 1, wave, lane);
+    int tb_next, tb_next_ahead;
+    u32x4 qop[4], qnext[4];
+    load_q(a, cur, c16, grp, qop);
+    int bad_cur = 0, bad_next = 0;
 
-  const uint32_t tsb = (uint32_t)a.Hkv * D * 2;           // bytes between consecutive slots
-  const uint32_t tile_bytes = 16 * tsb;
-  const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)kvh * D * 2;
-  const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)kvh * D * 2;
-  const uint32_t row_voff = 4 * grp * tsb + 16 * c16;     // tokens 4grp + r, bytes 16 c16 (whole rows)
-  u32x4 *kst = sm.kst[wave];
-
-  // issue the loads of chunk-local tile i (a zero-range descriptor past the chunk)
-  auto issue = [&](int c0, int i, int cn, u32x4 *kd, u32x4 *vd) {
-    const bool live = i < cn;
-    int phys = __builtin_amdgcn_readlane(tb, i & 63);
-    if (live && (unsigned)phys >= (unsigned)a.N) {
-      bad = 1;
-      phys = 0;
-    }
-    const int tok0 = (tile_lo + wave + kWaves * (c0 + i)) << 4;
-    const size_t off = ((size_t)phys * B + (tok0 % B)) * tsb;
-    const uint32_t range = live ? tile_bytes : 0u;
-    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kbase + off, range);
-    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vbase + off, range);
-    // K and V alike: instruction r reads whole 256-byte rows (tokens 4grp + r, 16 lanes
-    // per row), streamed past the caches (non-temporal).
+    // Loads of tile i of an item (zero-range descriptor past its live tiles).
+    auto load_tile = [&](const MItem &it, int i, int phys, u32x4 *kd, u32x4 *vd) {
+      const bool live = i < it.n_my;
+      const int tok0 = (it.tile_lo + wave + kWaves * i) << 4;
+      const size_t off = ((size_t)phys * B + (tok0 % B)) * tsb + (size_t)it.kvh * D * 2;
+      const uint32_t range = live ? tile_bytes : 0u;
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kpool + off, range);
+      const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vpool + off, range);
+      // K and V alike: instruction r reads whole 256-byte rows (tokens 4grp + r, 16 lanes
+      // per row), streamed past the caches (non-temporal).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, row_voff, r * tsb, kNontemporal);
+      for (int r = 0; r < 4; ++r) kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, row_voff, r * tsb, kNontemporal);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, row_voff, r * tsb, kNontemporal);
-  };
-
-  auto compute = [&](int i, u32x4 *kr, u32x4 *vr) {
-    const int tok0 = (tile_lo + wave + kWaves * i) << 4;
-    // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t sits at
-    // t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token, 16 chunks)
-    // and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of 64 banks.
-    // Lane (c16, grp) then holds token c16, chunks 4c + grp = head dims 32c + 8grp .. +7.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = 4 * grp + r;
-      kst[t * 16 + (c16 ^ t)] = kr[r];
-    }
-    u32x4 kop[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]), qop[c], sc, 0, 0, 0);
-
-    // scores of tokens tok0 + 4grp + r for head c16; positions past the end are masked
-    float sv[4], mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = tok0 + 4 * grp + r < t1;
-      sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
-      if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
-      mx = fmaxf(mx, sv[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = merge_weight(m, mnew);
-    float pr[4], ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - mnew);
-      ps += pr[r];
-    }
-    lsum = lsum * alpha + ps;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= alpha;
-    }
-    m = mnew;
-
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-    const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int w = j >> 1;
-      uint32_t a01, a23;
-      if (j & 1) {
-        a01 = (vr[0][w] >> 16) | (vr[1][w] & 0xffff0000u);
-        a23 = (vr[2][w] >> 16) | (vr[3][w] & 0xffff0000u);
-      } else {
-        a01 = (vr[0][w] & 0xffffu) | (vr[1][w] << 16);
-        a23 = (vr[2][w] & 0xffffu) | (vr[3][w] << 16);
+      for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, row_voff, r * tsb, kNontemporal);
+    };
+    // tile i of the current item
+    auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd) {
+      const bool live = i < cur.n_my;
+      if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
+        tb_cur = tb_ahead;
+        tb_ahead = table_chunk<B>(a, cur, (i >> 6) + 1, wave, lane);
       }
-      const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[j], 0, 0, 0);
-    }
-  };
-
-  // NBUF-deep ring of register buffers.  Pipeline step k issues tile k into buffer k % NBUF
-  // and computes tile k - (NBUF - 1); the loop is unrolled by NBUF so buffer indices are
-  // compile-time constants and every load sits inside the loop.  Issues past the chunk are
-  // zero-range (no memory access), computes outside [0, cn) are skipped by a wave-uniform
-  // branch, so the count of loads in flight is fixed and each wait covers one tile.
-  for (int c0 = 0; c0 < n_my; c0 += 64) {
-    if (c0 > 0) tb = table_chunk(c0);
-    const int cn = min(64, n_my - c0);
-    u32x4 kbuf[NBUF][4], vbuf[NBUF][4];
-    for (int k0 = 0; k0 < cn + NBUF - 1; k0 += NBUF) {
-#pragma unroll
-      for (int j = 0; j < NBUF; ++j) {
-        const int k = k0 + j;
-        issue(c0, k, cn, kbuf[j], vbuf[j]);
-        __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
-        const int kc = k - (NBUF - 1);
-        if (kc >= 0 && kc < cn) compute(c0 + kc, kbuf[(j + 1) % NBUF], vbuf[(j + 1) % NBUF]);
+      int phys = __builtin_amdgcn_readlane(tb_cur, i & 63);
+      if (live && (unsigned)phys >= (unsigned)a.N) {
+        bad_cur = 1;
+        phys = 0;
       }
+      load_tile(cur, i, phys, kd, vd);
+    };
+    // tile i (< NB - 1) of the next item
+    auto issue_next = [&](int i, int tb_nx, u32x4 *kd, u32x4 *vd) {
+      int phys = __builtin_amdgcn_readlane(tb_nx, i);
+      if (i < nxt.n_my && (unsigned)phys >= (unsigned)a.N) {
+        bad_next = 1;
+        phys = 0;
+      }
+      load_tile(nxt, i, phys, kd, vd);
+    };
+
+    float m = kNegInf, lsum = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int i, u32x4 *kr, u32x4 *vr) {
+      const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t sits
+      // at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token, 16
+      // chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of 64
+      // banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * grp + r;
+        kst[t * 16 + (c16 ^ t)] = kr[r];
+      }
+      u32x4 kop[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
+                                                     __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
+
+      // scores of tokens tok0 + 4grp + r for head c16; positions past the end are masked
+      float sv[4], mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = tok0 + 4 * grp + r < cur.t1;
+        sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
+        if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
+        mx = fmaxf(mx, sv[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      const float alpha = merge_weight(m, mnew);
+      float pr[4], ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - mnew);
+        ps += pr[r];
+      }
+      lsum = lsum * alpha + ps;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+      }
+      m = mnew;
+
+      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+      const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int wd = j >> 1;
+        uint32_t a01, a23;
+        if (j & 1) {
+          a01 = (vr[0][wd] >> 16) | (vr[1][wd] & 0xffff0000u);
+          a23 = (vr[2][wd] >> 16) | (vr[3][wd] & 0xffff0000u);
+        } else {
+          a01 = (vr[0][wd] & 0xffffu) | (vr[1][wd] << 16);
+          a23 = (vr[2][wd] & 0xffffu) | (vr[3][wd] << 16);
+        }
+        const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[j], 0, 0, 0);
+      }
+    };
+
+    // the stream's first tiles
+    u32x4 kbuf[NB][4], vbuf[NB][4];
+#pragma unroll
+    for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j]);
+
+    for (int k = 0;; ++k) {
+      // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
+      // copies into the current item's registers at the end of this iteration, so those
+      // copies never wait on memory.
+      nxt = item_at<NB>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
+      tb_next = table_chunk<B>(a, nxt, 0, wave, lane);
+      tb_next_ahead = table_chunk<B>(a, nxt, 1, wave, lane);
+      load_q(a, nxt, c16, grp, qnext);
+      // fetch it_{k+2} while it_k runs (its value is first used at the merge below)
+      const bool fetch = a.persistent && tid == 0 && wn < total;
+      unsigned fetched = 0u;
+      if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
+
+      // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
+      // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
+      // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
+      // entries sits only there.
+      // The first body is a copy of its own too: its waits count the loads and stores
+      // issued since this item's first tiles (the merge, the next item's table and q), so
+      // it does not wait for more tiles than the one it computes.
+      auto body = [&](int x) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          issue_cur(x + j + NB - 1, kbuf[(j + NB - 1) % NB], vbuf[(j + NB - 1) % NB]);
+          __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
+          if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j]);
+        }
+      };
+      int x = 0;
+      if (cur.n_pad > NB) {
+        body(0);
+        for (x = NB; x < cur.n_pad - NB; x += NB) body(x);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (j == 0)
+          issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1]);
+        else
+          issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j]);
+      }
+
+      // merge the waves' states of it_k (the next item's first loads are in flight)
+      float lh = lsum + __shfl_xor(lsum, 16);
+      lh += __shfl_xor(lh, 32);
+      const int mb = k & 1;
+      if (grp == 0) {
+        sm.m[mb][c16][wave] = m;
+        sm.l[mb][c16][wave] = lh;
+      }
+      if (lane == 0) sm.bad[mb][wave] = bad_cur;
+      {
+        float *dst = &sm.o[mb][wave][c16][32 * grp];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
+        }
+      }
+      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(gridDim.x + fetched) : total;
+      __syncthreads();
+      if (cur.fill == 0)
+        mfma_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
+      else if (cur.fill != 3)
+        fill_group<uint16_t, D>(a, cur.s, cur.kvh * a.g, a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
+      if (wn >= total) break;
+
+      // advance the stream by one item
+      w = wn;
+      wn = a.persistent ? sm.nextw[k & 1] : total;
+      cur = nxt;
+      tb_cur = tb_next;
+      tb_ahead = tb_next_ahead;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
+      bad_cur = bad_next;
+      bad_next = 0;
+      m = kNegInf;
+      lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   }
-
-  float lh = lsum + __shfl_xor(lsum, 16);
-  lh += __shfl_xor(lh, 32);
-  if (grp == 0) {
-    sm_m[wave][c16] = m;
-    sm_l[wave][c16] = lh;
-  }
-  if (lane == 0) sm_bad[wave] = bad;
-  {
-    float *dst = &sm_o[wave][c16][32 * grp];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
-    }
-  }
-  __syncthreads();
-  finish_group<uint16_t, D, 16, OS>(a, s, kvh, p, single, sm_m, sm_l, sm_o, sm_bad);
+  if (a.persistent) queue_done(a.queue);
 }
-
-template <int B, int NBUF>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
-  __shared__ MfmaSmem sm;
-  __shared__ SchedSmem sc;
-  extern __shared__ int sm_dyn[];
-  run_items(a, sc, sm_dyn, [&](int s, int p, int kvh, int ctx) { mfma_item<B, NBUF>(a, s, p, kvh, ctx, sm); });
-}
-
 // ---------------------------------------------------------------------------
 // Vector path.  T = float or uint16_t (bf16).  Each token row of a KV head is
 // D*sizeof(T) bytes = LPT lanes x 16 bytes; a wave covers TPW = 64 / LPT rows at once.
@@ -706,20 +1058,22 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
   __shared__ f32x4 sm_acc[kThreads];
   __shared__ float red[kWaves];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
-  if (h == 0 && s == 0 && tid == 0) a.queue[0] = 0u;   // pass 1 is complete: reset its work queue
   const int ctx = a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
   const int np = (ctx + a.P - 1) / a.P;
   const size_t base = ((size_t)s * a.Hq + h) * a.max_parts;
 
+  // (m_p, l_p) of this head: entry 2j of item (s, kvh, p)'s line
+  const int kvh = h / a.g, j = h % a.g;
+  const float *ml = a.ws_ml + ((size_t)s * a.Hkv + kvh) * a.max_parts * 32 + 2 * j;
   float mx = kNegInf;
-  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, a.ws_m[base + i]);
+  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ml[(size_t)i * 32]);
   const float M = block_reduce(mx, true, red);
   float ls = 0.f;
   for (int i = tid; i < np; i += kThreads) {
-    const float w = merge_weight(a.ws_m[base + i], M);
+    const float w = merge_weight(ml[(size_t)i * 32], M);
     sm_w[i] = w;
-    ls += w * a.ws_l[base + i];
+    ls += w * ml[(size_t)i * 32 + 1];
   }
   const float L = block_reduce(ls, false, red);   // its barriers also publish sm_w
 
@@ -739,11 +1093,6 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
   }
 }
 
-// Queue reset when no merge kernel follows pass 1.
-__global__ void queue_reset_kernel(unsigned *queue) {
-  if (threadIdx.x == 0) queue[0] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -755,7 +1104,7 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   if (D != 64 && D != 128) return PKV_PATH_NONE;
   if (B != 4 && B != 8 && B != 16 && B != 32) return PKV_PATH_NONE;
   const int g = Hq / Hkv;
-  if (dt == PKV_DTYPE_BF16 && D == 128 && (B == 16 || B == 32) && g >= 2 && g <= 16) return PKV_PATH_MFMA;
+  if (dt == PKV_DTYPE_BF16 && D == 128 && (B == 16 || B == 32) && g <= 16) return PKV_PATH_MFMA;
   return vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
 }
 
@@ -822,7 +1171,8 @@ extern "C" size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_hea
     return kQueueBytes;
   const int64_t np = parts_for(max_context_len, partition_size);
   if (np <= 1) return kQueueBytes;
-  return kQueueBytes + (size_t)num_seqs * num_heads * np * (head_dim + 2) * sizeof(float);
+  // partial outputs [S, Hq, np, D] and (m, l) lines [S, Hkv, np, 32] (sized for Hkv = Hq)
+  return kQueueBytes + (size_t)num_seqs * num_heads * np * (head_dim + 32) * sizeof(float);
 }
 
 extern "C" pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
@@ -843,6 +1193,8 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   if (partition_size > 0 && partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  // token and table-byte offsets are 32-bit inside the kernels
+  if (max_context_len > (1 << 30) || max_blocks_per_seq > (1 << 29)) return PKV_ERR_UNSUPPORTED;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
@@ -865,8 +1217,7 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   const size_t nparts_total = (size_t)num_seqs * num_heads * (size_t)np;
   a.queue = reinterpret_cast<unsigned *>(workspace);
   a.ws_o = np > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kQueueBytes) : nullptr;
-  a.ws_m = np > 1 ? a.ws_o + nparts_total * head_dim : nullptr;
-  a.ws_l = np > 1 ? a.ws_m + nparts_total : nullptr;
+  a.ws_ml = np > 1 ? a.ws_o + nparts_total * head_dim : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.Hq = num_heads;
@@ -888,7 +1239,7 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   int64_t grid = items;
   a.persistent = 0;
   if (num_seqs <= kMaxSchedSeqs) {
-    dyn_lds = 2 * (size_t)num_seqs * sizeof(int);
+    dyn_lds = (path == PKV_PATH_MFMA ? 3 : 2) * (size_t)num_seqs * sizeof(int);
     const int resident = resident_workgroups(fn, dyn_lds);
     if (resident > 0) {
       a.persistent = 1;
@@ -902,10 +1253,6 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
       hipSuccess)
     return PKV_ERR_HIP;
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
-  if (np <= 1 && a.persistent) {
-    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, a.queue);
-    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
-  }
   if (np > 1) {
     const dim3 rgrid((unsigned)num_heads, (unsigned)num_seqs);
     if (bf16) {

@@ -43,17 +43,20 @@ def test_status_strings(L):
 
 
 def test_workspace_size(L):
-    # 256-byte work-queue header + S * Hq * ceil(max_ctx / P) * (D + 2) fp32 partials when split
-    assert binding.attention_workspace_size(8, 32, 128, 131072, 512) == 256 + 8 * 32 * 256 * 130 * 4
+    # 256-byte work-queue header + S * Hq * ceil(max_ctx / P) * (D + 32) fp32 when split:
+    # D partial outputs per (sequence, head, partition) and one 128-byte (m, l) line per item
+    assert binding.attention_workspace_size(8, 32, 128, 131072, 512) == 256 + 8 * 32 * 256 * 160 * 4
     assert binding.attention_workspace_size(8, 32, 128, 100, 512) == 256    # one partition
     assert binding.attention_workspace_size(8, 32, 128, 1000, 0) == 256     # no split
-    assert binding.attention_workspace_size(2, 4, 64, 513, 512) == 256 + 2 * 4 * 2 * 66 * 4
+    assert binding.attention_workspace_size(2, 4, 64, 513, 512) == 256 + 2 * 4 * 2 * 96 * 4
 
 
 def test_path_selection(L):
     assert binding.attention_path(64, 8, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA
     assert binding.attention_path(32, 8, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA
-    assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_VECTOR
+    assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA     # g = 1 too
+    assert binding.attention_path(16, 1, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA      # g = 16
+    assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_F32) == PKV_PATH_VECTOR
     assert binding.attention_path(4, 4, 64, 4, PKV_DTYPE_F32) == PKV_PATH_VECTOR
     assert binding.attention_path(32, 8, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_VECTOR
     assert binding.attention_path(64, 4, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE   # g = 16 off the MFMA path

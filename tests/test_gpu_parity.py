@@ -172,7 +172,9 @@ SHAPES = [
     ("bf16", 4, 8, 8, 64, 4, (1, 200)),       # vector, D = 64, B = 4
     ("bf16", 4, 16, 2, 64, 8, (1, 200)),      # vector, g = 8
     ("bf16", 4, 6, 2, 128, 8, (1, 200)),      # vector, g = 3, B = 8
-    ("bf16", 4, 8, 8, 128, 32, (1, 300)),     # vector MHA, B = 32
+    ("bf16", 4, 8, 8, 128, 32, (1, 300)),     # MHA (g = 1) on the MFMA path, B = 32
+    ("bf16", 4, 8, 8, 128, 8, (1, 300)),      # vector MHA, D = 128, B = 8
+    ("bf16", 3, 4, 4, 128, 16, (4200, 9000)), # g = 1, MFMA, more than 64 tiles per wave
     ("f32", 4, 8, 8, 128, 16, (1, 200)),      # fp32, D = 128 (32 lanes per row)
     ("f32", 4, 8, 2, 64, 8, (1, 200)),        # fp32 GQA on the vector path
     ("f32", 3, 5, 5, 64, 32, (1, 200)),
