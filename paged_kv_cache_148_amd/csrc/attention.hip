@@ -730,11 +730,6 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       tb_next = table_chunk<B>(a, nxt, 0, wave, lane);
       tb_next_ahead = table_chunk<B>(a, nxt, 1, wave, lane);
       load_q(a, nxt, c16, grp, qnext);
-      // fetch it_{k+2} while it_k runs (its value is first used at the merge below)
-      const bool fetch = a.persistent && tid == 0 && wn < total;
-      unsigned fetched = 0u;
-      if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
-
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
       // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
       // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
@@ -755,6 +750,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         body(0);
         for (x = NB; x < cur.n_pad - NB; x += NB) body(x);
       }
+      // Take it_{k+2} from the queue now, NB tiles before this item ends (its index is first
+      // read at the merge below).  Taking it later than at the item's start keeps a slow
+      // workgroup from claiming a long item early that a faster one would finish sooner.
+      const bool fetch = a.persistent && tid == 0 && wn < total;
+      unsigned fetched = 0u;
+      if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (j == 0)
