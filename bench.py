@@ -15,6 +15,7 @@ the written / copied rows), not what the implementation happens to move.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -71,11 +72,24 @@ def measured_traffic(workload: str, per_launch_alg: int):
     return rec.get("hbm_bytes_per_launch")
 
 
-def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered"):
+def block_stats(cfg, step) -> dict:
+    """Internal fragmentation of the step's block allocation (slots allocated but past the
+    context, over all allocated slots) and block-table length."""
+    B = cfg.block_size
+    ctx = step.context_lens.astype(np.int64)
+    blocks = -(-ctx // B)
+    return {"block_size": B, "internal_frag": float((blocks * B - ctx).sum() / max(1, int((blocks * B).sum()))),
+            "table_entries_mean": float(blocks.mean()), "table_entries_max": int(blocks.max())}
+
+
+def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered",
+            block_size: int | None = None):
     import torch
     from paged_kv_cache_148_amd import batch, binding
 
     cfg = workloads.CONFIGS[name]
+    if block_size is not None and block_size != cfg.block_size:
+        cfg = dataclasses.replace(cfg, block_size=block_size)
     t_gen = time.time()
     wl = workloads.make_workload(cfg)
     if layout == "contiguous":
@@ -139,6 +153,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
         "copy_pairs": int(n_pairs), "path": binding.attention_path(cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                                                                     cfg.block_size, 1 if bf16 else 0),
         "input_gen_s": gen_s,
+        **block_stats(cfg, step),
     }
     if name == "fork_cow":
         shared = (cfg.ctx[1] // cfg.block_size) * cfg.block_size
@@ -218,6 +233,10 @@ def main():
                     help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
     ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous"],
                     help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="run the workload with this block size instead of its configured one")
+    ap.add_argument("--sweep-block-size", action="store_true",
+                    help="time the workload at block sizes 8..128 and print one JSON line of the sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
@@ -233,7 +252,22 @@ def main():
 
     main_part = PARTITION[args.workload] if args.partition is None else args.partition
     which = "steady"
-    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout)
+    if args.sweep_block_size:
+        sweep = []
+        for B in (8, 16, 32, 64, 128):
+            r, _, _ = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, B)
+            keep = ("block_size", "internal_frag", "table_entries_mean", "table_entries_max", "path", "pool_blocks",
+                    "attention_us_mean", "attention_us_p10", "attention_us_p90", "us_per_step", "kv_gbs_attention",
+                    "attention_alg_gbs", "attention_hbm_frac")
+            sweep.append({k: (round(r[k], 4) if isinstance(r[k], float) else r[k]) for k in keep})
+            print(f"[bench] {args.workload} B={B}: attention {r['attention_us_mean']:.1f} us, "
+                  f"{r['attention_alg_gbs']:.0f} GB/s, internal fragmentation {100 * r['internal_frag']:.2f}%",
+                  file=sys.stderr, flush=True)
+        print(json.dumps({"block_size_sweep": args.workload, "partition_size": main_part, "layout": args.layout,
+                          "steps": args.steps, "warmup": args.warmup, "results": sweep,
+                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return
+    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size)
     print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step, attention {res['attention_us_mean']:.1f} us, "
           f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
@@ -267,7 +301,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q/K/V, seeded shuffled block pool)",
         "config": {"workload": f"{args.workload}: {cfg.description}", "num_seqs": cfg.num_seqs,
                    "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
-                   "block_size": cfg.block_size, "partition_size": main_part, "sum_ctx": res["sum_ctx"],
+                   "block_size": res["block_size"], "partition_size": main_part, "sum_ctx": res["sum_ctx"],
                    "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
         "seqs_per_s": round(res["seqs_per_s"], 1),

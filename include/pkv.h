@@ -27,10 +27,11 @@
  * failure returns PKV_ERR_HIP.  Device-resident values cannot be checked on the
  * host; how each kernel treats out-of-range device values is stated per call.
  *
- * Supported shapes: head_dim in {64, 128}; block_size in {4, 8, 16, 32};
- * num_heads % num_kv_heads == 0; dtype fp32 or bf16.  Attention additionally
- * needs g = num_heads / num_kv_heads <= 8, or g <= 16 on the bf16 matrix-core
- * path (head_dim 128, block_size 16 or 32).  pkv_attention_path reports which.
+ * Supported shapes: head_dim in {64, 128}; block_size in {4, 8, 16, 32, 64, 128};
+ * num_heads % num_kv_heads == 0; dtype fp32 or bf16.  Attention runs on the bf16
+ * matrix-core path for head_dim 128 and block_size >= 16 (g = num_heads /
+ * num_kv_heads <= 16), otherwise on the vector path, which needs block_size <= 32
+ * and g <= 8.  pkv_attention_path reports which.
  * All data pointers must be 16-byte aligned, index arrays 4- or 8-byte aligned.
  */
 #ifndef PKV_H

@@ -25,13 +25,13 @@
 // LDS fall back to one workgroup per possible item.
 //
 // Two pass-1 kernels:
-//   attn_mfma_kernel  (bf16, D = 128, B in {16, 32}, 1 <= g <= 16): a 16-token tile of
+//   attn_mfma_kernel  (bf16, D = 128, every block size, 1 <= g <= 16): a 16-token tile of
 //     K times the group's Q^T on v_mfma_f32_16x16x32_bf16 gives the score tile; the
 //     probabilities stay in the MFMA result layout and feed v_mfma_f32_16x16x16_bf16
 //     against V^T for P.V.  The head dimension of the P.V product is permuted so that
 //     each lane's V operand is one 16-byte row piece of 4 tokens, regrouped in
 //     registers (no LDS round trip for V).
-//   attn_vec_kernel   (everything else: fp32, D = 64, small blocks): one token
+//   attn_vec_kernel   (everything else: fp32, D = 64): one token
 //     row per D*e/16 lanes, 16-byte loads along head_dim, q.k as fp32 FMAs on exactly
 //     widened elements, row sums by DPP.
 // Scores carry scale * log2(e) so every exponential is a hardware exp2.
@@ -241,7 +241,7 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: bf16, D = 128, B in {16, 32}, a group of 1 to 16 query heads.
+// MFMA path: bf16, D = 128, any block size (4 .. 128), a group of 1 to 16 query heads.
 //
 // Lane l of a wave: c16 = l % 16, grp = l / 16.
 //   QK  (v_mfma_f32_16x16x32_bf16, A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]):
@@ -288,7 +288,7 @@ struct MfmaSmem {
 // One work item as a wave sees it.  Every field is wave-uniform.
 struct MItem {
   int s, p, kvh;
-  int t1;        // end of the attended token range (exclusive)
+  int t0, t1;    // attended token range [t0, t1)
   int tile_lo;   // first 16-token tile of the partition
   int n_my;      // this wave's live tiles: tile_lo + wave + kWaves * i, i < n_my
   int n_pad;     // loop length: n_my rounded up to a multiple of NB, at least NB
@@ -423,6 +423,7 @@ __device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int 
   it.p = p;
   it.kvh = kvh;
   it.tile_lo = (p * a.P) >> 4;
+  it.t0 = p * a.P;
   it.t1 = 0;
   it.n_my = 0;
   it.single = 0;
@@ -444,21 +445,31 @@ __device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int 
 // An empty item: what the stream holds past the workgroup's last item.
 __device__ __forceinline__ MItem no_item() {
   MItem it;
-  it.s = it.p = it.kvh = it.t1 = it.tile_lo = it.n_my = it.single = 0;
+  it.s = it.p = it.kvh = it.t0 = it.t1 = it.tile_lo = it.n_my = it.single = 0;
   it.n_pad = 0;
   it.fill = 3;
   return it;
 }
 
-// Block-table entries of tiles 64c .. 64c + 63 of an item, one per lane (zero past the
-// table row or for an item with nothing to attend).
+// Blocks that one 16-token tile spans: 16 / B for blocks of 4 or 8 slots, else 1.
 template <int B>
-__device__ __forceinline__ int table_chunk(const AttnArgs &a, const MItem &it, int c, int wave, int lane) {
+constexpr int tile_blocks() { return B < 16 ? 16 / B : 1; }
+
+// Block-table entries of tiles 64c .. 64c + 63 of an item, one per lane: entry h of each
+// tile's blocks (zero past the table row or for an item with nothing to attend).
+template <int B>
+__device__ __forceinline__ int table_chunk(const AttnArgs &a, const MItem &it, int c, int h, int wave, int lane) {
   const bool live = it.fill == 0 && 64 * c < it.n_my;
   const __amdgpu_buffer_rsrc_t r =
       buf_rsrc(a.tables + (size_t)it.s * a.max_blocks, live ? (uint32_t)a.max_blocks * 4u : 0u);
   const int tok = (it.tile_lo + wave + kWaves * (64 * c + lane)) << 4;
-  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (tok / B) * 4, 0, 0);
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (tok / B + h) * 4, 0, 0);
+}
+template <int B>
+__device__ __forceinline__ void table_chunks(const AttnArgs &a, const MItem &it, int c, int wave, int lane,
+                                             int *tb) {
+#pragma unroll
+  for (int h = 0; h < tile_blocks<B>(); ++h) tb[h] = table_chunk<B>(a, it, c, h, wave, lane);
 }
 
 // The Q^T operand of an item: head c16 of the KV head's group (zero columns past g).
@@ -479,6 +490,7 @@ __device__ __forceinline__ MItem uniform(MItem it) {
   it.s = __builtin_amdgcn_readfirstlane(it.s);
   it.p = __builtin_amdgcn_readfirstlane(it.p);
   it.kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  it.t0 = __builtin_amdgcn_readfirstlane(it.t0);
   it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
   it.tile_lo = __builtin_amdgcn_readfirstlane(it.tile_lo);
   it.n_my = __builtin_amdgcn_readfirstlane(it.n_my);
@@ -567,7 +579,6 @@ __device__ __forceinline__ void mfma_finish(const AttnArgs &a, const MItem &it, 
 template <int B, int NB>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   constexpr int D = 128;
-  constexpr int OS = kMfmaOS;
   __shared__ MfmaSmem sm;
   extern __shared__ int sm_dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -593,57 +604,86 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     MItem cur = item_at<NB>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
     MItem nxt;
 
+    // Token of a tile row.  Load instruction r gives lane group grp the tile token
+    //   tok(grp, r) = blk * B + (4 / BPT) * grp + r % (4 / BPT),   blk = r / (4 / BPT),
+    // BPT = blocks per tile: with blocks of 16 or more it is 4grp + r; with smaller blocks
+    // every instruction stays inside one block (blk), so one buffer descriptor serves it.
+    // The MFMA row of that token is 4grp + r throughout (K staging, scores, P, V alike), so
+    // the only effect is the order of the tile's tokens in the P.V sum.
+    constexpr int BPT = tile_blocks<B>();
+    constexpr int RPI = 4 / BPT;   // consecutive load instructions per block
     const uint32_t tsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive slots
-    const uint32_t tile_bytes = 16 * tsb;
+    const uint32_t blk_bytes = (BPT == 1 ? 16 : B) * tsb;   // range of one descriptor
     const char *kpool = reinterpret_cast<const char *>(a.k);
     const char *vpool = reinterpret_cast<const char *>(a.v);
-    const uint32_t row_voff = 4 * grp * tsb + 16 * c16;   // tokens 4grp + r, bytes 16 c16 (whole rows)
+    const uint32_t row_voff = RPI * grp * tsb + 16 * c16;   // whole 256-byte rows, bytes 16 c16
     u32x4 *kst = sm.kst[wave];
 
     // registers of the stream: table chunks (current item: the chunk being issued and the
-    // one after it; next item: its first two), q operands, validity flags
-    int tb_cur = table_chunk<B>(a, cur, 0, wave, lane);
-    int tb_ahead = table_chunk<B>(a, cur, 1, wave, lane);
-    int tb_next, tb_next_ahead;
+    // one after it; next item: its first two; one register per block of a tile), q operands,
+    // validity flags
+    int tb_cur[BPT], tb_ahead[BPT], tb_next[BPT], tb_next_ahead[BPT];
+    table_chunks<B>(a, cur, 0, wave, lane, tb_cur);
+    table_chunks<B>(a, cur, 1, wave, lane, tb_ahead);
     u32x4 qop[4], qnext[4];
     load_q(a, cur, c16, grp, qop);
     int bad_cur = 0, bad_next = 0;
 
-    // Loads of tile i of an item (zero-range descriptor past its live tiles).
-    auto load_tile = [&](const MItem &it, int i, int phys, u32x4 *kd, u32x4 *vd) {
+    // Loads of tile i of an item (zero-range descriptors past its live tiles).
+    auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd) {
       const bool live = i < it.n_my;
       const int tok0 = (it.tile_lo + wave + kWaves * i) << 4;
-      const size_t off = ((size_t)phys * B + (tok0 % B)) * tsb + (size_t)it.kvh * D * 2;
-      const uint32_t range = live ? tile_bytes : 0u;
-      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kpool + off, range);
-      const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vpool + off, range);
-      // K and V alike: instruction r reads whole 256-byte rows (tokens 4grp + r, 16 lanes
-      // per row), streamed past the caches (non-temporal).
+      __amdgpu_buffer_rsrc_t rk[BPT], rv[BPT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, row_voff, r * tsb, kNontemporal);
+      for (int h = 0; h < BPT; ++h) {
+        // a block of the tile that lies wholly past the range (its table entry is padding) or
+        // a tile past the item's live ones: zero-range descriptor, no memory access
+        const uint32_t range = live && tok0 + h * B < it.t1 ? blk_bytes : 0u;
+        // the tile's rows in block h (B >= 16: the 16 rows from offset tok0 % B)
+        const size_t off = ((size_t)phys[h] * B + (BPT == 1 ? tok0 % B : 0)) * tsb + (size_t)it.kvh * D * 2;
+        rk[h] = buf_rsrc(kpool + off, range);
+        rv[h] = buf_rsrc(vpool + off, range);
+      }
+      // K and V alike: instruction r reads whole 256-byte rows (16 lanes per row), streamed
+      // past the caches (non-temporal).
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, row_voff, r * tsb, kNontemporal);
+      for (int r = 0; r < 4; ++r)
+        kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
     };
     // tile i of the current item
     auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd) {
       const bool live = i < cur.n_my;
       if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
-        tb_cur = tb_ahead;
-        tb_ahead = table_chunk<B>(a, cur, (i >> 6) + 1, wave, lane);
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) tb_cur[h] = tb_ahead[h];
+        table_chunks<B>(a, cur, (i >> 6) + 1, wave, lane, tb_ahead);
       }
-      int phys = __builtin_amdgcn_readlane(tb_cur, i & 63);
-      if (live && (unsigned)phys >= (unsigned)a.N) {
-        bad_cur = 1;
-        phys = 0;
+      const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      int phys[BPT];
+#pragma unroll
+      for (int h = 0; h < BPT; ++h) {
+        phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
+        if ((unsigned)phys[h] >= (unsigned)a.N) {
+          if (live && tok0 + h * B < cur.t1) bad_cur = 1;   // an entry the range reads
+          phys[h] = 0;
+        }
       }
       load_tile(cur, i, phys, kd, vd);
     };
     // tile i (< NB - 1) of the next item
-    auto issue_next = [&](int i, int tb_nx, u32x4 *kd, u32x4 *vd) {
-      int phys = __builtin_amdgcn_readlane(tb_nx, i);
-      if (i < nxt.n_my && (unsigned)phys >= (unsigned)a.N) {
-        bad_next = 1;
-        phys = 0;
+    auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd) {
+      const int tok0 = (nxt.tile_lo + wave + kWaves * i) << 4;
+      int phys[BPT];
+#pragma unroll
+      for (int h = 0; h < BPT; ++h) {
+        phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
+        if ((unsigned)phys[h] >= (unsigned)a.N) {
+          if (i < nxt.n_my && tok0 + h * B < nxt.t1) bad_next = 1;
+          phys[h] = 0;
+        }
       }
       load_tile(nxt, i, phys, kd, vd);
     };
@@ -673,11 +713,12 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
                                                      __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
 
-      // scores of tokens tok0 + 4grp + r for head c16; positions past the end are masked
+      // scores of tile rows 4grp + r for head c16; positions outside [t0, t1) are masked
       float sv[4], mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool ok = tok0 + 4 * grp + r < cur.t1;
+        const int tk = tok0 + (r / RPI) * B + RPI * grp + r % RPI;
+        const bool ok = tk >= cur.t0 && tk < cur.t1;
         sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
         if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
         mx = fmaxf(mx, sv[r]);
@@ -727,8 +768,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       // copies into the current item's registers at the end of this iteration, so those
       // copies never wait on memory.
       nxt = item_at<NB>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
-      tb_next = table_chunk<B>(a, nxt, 0, wave, lane);
-      tb_next_ahead = table_chunk<B>(a, nxt, 1, wave, lane);
+      table_chunks<B>(a, nxt, 0, wave, lane, tb_next);
+      table_chunks<B>(a, nxt, 1, wave, lane, tb_next_ahead);
       load_q(a, nxt, c16, grp, qnext);
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
       // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
@@ -795,8 +836,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       w = wn;
       wn = a.persistent ? sm.nextw[k & 1] : total;
       cur = nxt;
-      tb_cur = tb_next;
-      tb_ahead = tb_next_ahead;
+#pragma unroll
+      for (int h = 0; h < BPT; ++h) {
+        tb_cur[h] = tb_next[h];
+        tb_ahead[h] = tb_next_ahead[h];
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
       bad_cur = bad_next;
@@ -1103,10 +1147,10 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PKV_PATH_NONE;
   if (dt != PKV_DTYPE_F32 && dt != PKV_DTYPE_BF16) return PKV_PATH_NONE;
   if (D != 64 && D != 128) return PKV_PATH_NONE;
-  if (B != 4 && B != 8 && B != 16 && B != 32) return PKV_PATH_NONE;
+  if (B != 4 && B != 8 && B != 16 && B != 32 && B != 64 && B != 128) return PKV_PATH_NONE;
   const int g = Hq / Hkv;
-  if (dt == PKV_DTYPE_BF16 && D == 128 && (B == 16 || B == 32) && g <= 16) return PKV_PATH_MFMA;
-  return vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
+  if (dt == PKV_DTYPE_BF16 && D == 128 && g <= 16) return PKV_PATH_MFMA;
+  return B <= 32 && vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
 }
 
 typedef void (*Pass1Fn)(AttnArgs);
@@ -1132,7 +1176,16 @@ static Pass1Fn vec_fn(int g, int B) {
 }
 
 static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g) {
-  if (path == PKV_PATH_MFMA) return B == 16 ? attn_mfma_kernel<16, kMfmaDepth> : attn_mfma_kernel<32, kMfmaDepth>;
+  if (path == PKV_PATH_MFMA) {
+    switch (B) {
+      case 4: return attn_mfma_kernel<4, kMfmaDepth>;
+      case 8: return attn_mfma_kernel<8, kMfmaDepth>;
+      case 16: return attn_mfma_kernel<16, kMfmaDepth>;
+      case 32: return attn_mfma_kernel<32, kMfmaDepth>;
+      case 64: return attn_mfma_kernel<64, kMfmaDepth>;
+      default: return attn_mfma_kernel<128, kMfmaDepth>;
+    }
+  }
   if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
   return D == 128 ? vec_fn<float, 128>(g, B) : vec_fn<float, 64>(g, B);
 }

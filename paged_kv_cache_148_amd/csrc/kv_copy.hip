@@ -67,7 +67,9 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(u32x4 *__rest
 
 static bool shape_ok(int32_t block_size, int32_t num_kv_heads, int32_t head_dim) {
   return (head_dim == 64 || head_dim == 128) &&
-         (block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32) && num_kv_heads >= 1;
+         (block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 ||
+          block_size == 128) &&
+         num_kv_heads >= 1;
 }
 
 static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

@@ -58,11 +58,18 @@ def test_path_selection(L):
     assert binding.attention_path(16, 1, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA      # g = 16
     assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_F32) == PKV_PATH_VECTOR
     assert binding.attention_path(4, 4, 64, 4, PKV_DTYPE_F32) == PKV_PATH_VECTOR
-    assert binding.attention_path(32, 8, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_VECTOR
-    assert binding.attention_path(64, 4, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE   # g = 16 off the MFMA path
+    assert binding.attention_path(32, 8, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_MFMA    # blocks below a tile
+    assert binding.attention_path(32, 8, 128, 4, PKV_DTYPE_BF16) == PKV_PATH_MFMA
+    assert binding.attention_path(32, 8, 64, 8, PKV_DTYPE_BF16) == PKV_PATH_VECTOR   # head_dim 64
+    assert binding.attention_path(64, 4, 64, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE    # g = 16 off the MFMA path
+    assert binding.attention_path(64, 2, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE   # g = 32
     assert binding.attention_path(6, 4, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE   # 6 % 4 != 0
     assert binding.attention_path(8, 8, 96, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE    # head_dim
-    assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_BF16) == PKV_PATH_NONE   # block size
+    assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_BF16) == PKV_PATH_MFMA   # large blocks: MFMA only
+    assert binding.attention_path(64, 8, 128, 128, PKV_DTYPE_BF16) == PKV_PATH_MFMA
+    assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_F32) == PKV_PATH_NONE    # no vector path past 32
+    assert binding.attention_path(8, 8, 64, 128, PKV_DTYPE_BF16) == PKV_PATH_NONE
+    assert binding.attention_path(8, 8, 128, 256, PKV_DTYPE_BF16) == PKV_PATH_NONE  # block size
     assert binding.attention_path(8, 8, 128, 16, 7) == PKV_PATH_NONE                # dtype
 
 

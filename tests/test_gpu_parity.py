@@ -121,6 +121,30 @@ def test_copy_blocks_random_pairs_bit_exact(name):
     del torch
 
 
+@pytest.mark.parametrize("B", [64, 128])
+def test_write_and_copy_large_blocks_bit_exact(B):
+    # the block-size sweep's large blocks: slot-mapped write, then random whole-block copies
+    cfg = workloads.Config("bigblock", "bf16", 6, 16, 4, 128, B, ("uniform", 1, 3 * B), seed=200 + B)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    _say("write large blocks", B)
+    H.gpu_step(wl, step, d, 0, do_attn=False)
+    _, kc, vc, _ = H.oracle_step(wl, "steady", attend=False)   # the oracle's own slots
+    assert H.bits(d["k_cache"]).tobytes() == kc.tobytes()
+    assert H.bits(d["v_cache"]).tobytes() == vc.tobytes()
+    rng = np.random.default_rng(B)
+    perm = rng.permutation(wl.num_blocks)
+    npairs = wl.num_blocks // 2
+    pairs = np.stack([perm[:npairs], perm[npairs:2 * npairs]], axis=1).astype(np.int64)
+    d["copy_pairs"] = pbatch.to_torch(pairs, "cuda")
+    _say("copy large blocks", B, pairs.shape)
+    H.gpu_step(wl, step, d, 0, do_write=False, do_attn=False)
+    oracle.copy_blocks(kc, vc, pairs)
+    assert H.bits(d["k_cache"]).tobytes() == kc.tobytes()
+    assert H.bits(d["v_cache"]).tobytes() == vc.tobytes()
+
+
 # ---------------------------------------------------------------------------
 # attention on the configurations (sizes the oracle finishes in seconds)
 # ---------------------------------------------------------------------------
@@ -171,10 +195,14 @@ SHAPES = [
     ("bf16", 4, 24, 8, 128, 32, (1, 400)),    # g = 3, B = 32
     ("bf16", 4, 8, 8, 64, 4, (1, 200)),       # vector, D = 64, B = 4
     ("bf16", 4, 16, 2, 64, 8, (1, 200)),      # vector, g = 8
-    ("bf16", 4, 6, 2, 128, 8, (1, 200)),      # vector, g = 3, B = 8
+    ("bf16", 4, 6, 2, 128, 8, (1, 200)),      # MFMA, g = 3, B = 8: two blocks per tile
+    ("bf16", 4, 8, 2, 128, 4, (1, 200)),      # MFMA, g = 4, B = 4: four blocks per tile
     ("bf16", 4, 8, 8, 128, 32, (1, 300)),     # MHA (g = 1) on the MFMA path, B = 32
-    ("bf16", 4, 8, 8, 128, 8, (1, 300)),      # vector MHA, D = 128, B = 8
+    ("bf16", 4, 8, 8, 128, 8, (1, 300)),      # MHA on the MFMA path, B = 8
     ("bf16", 3, 4, 4, 128, 16, (4200, 9000)), # g = 1, MFMA, more than 64 tiles per wave
+    ("bf16", 5, 32, 4, 128, 64, (1, 700)),    # B = 64, g = 8
+    ("bf16", 4, 8, 8, 128, 128, (1, 900)),    # B = 128, g = 1
+    ("bf16", 3, 16, 2, 128, 128, (1, 2600)),  # B = 128, g = 8, more than 64 tiles per wave
     ("f32", 4, 8, 8, 128, 16, (1, 200)),      # fp32, D = 128 (32 lanes per row)
     ("f32", 4, 8, 2, 64, 8, (1, 200)),        # fp32 GQA on the vector path
     ("f32", 3, 5, 5, 64, 32, (1, 200)),
@@ -187,7 +215,8 @@ def test_shape_sweep_parity(shape):
     cfg = workloads.Config("sweep", dt, S, Hq, Hkv, D, B, ("uniform", lo, hi), seed=100 + Hq + D + B)
     wl = workloads.make_workload(cfg)
     step = pbatch.step_for(wl)
-    for P in (0, 4 * B if B >= 16 else 64):
+    # below 16 slots per block also a partition that is not a multiple of the 16-token tile
+    for P in (0, 4 * B if B >= 16 else 64) + ((3 * B,) if B < 16 else ()):
         _say("sweep", shape, "P", P)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P)
@@ -275,6 +304,35 @@ def test_unread_slots_and_table_padding_never_read(name, P):
     d2 = H.upload(wl, step)
     H.gpu_step(wl, step, d2, P)
     assert H.bits(d2["out"]).tobytes() == clean.tobytes()
+
+
+@pytest.mark.parametrize("B", [4, 8])
+def test_small_blocks_padding_never_read(B):
+    # several blocks per 16-token tile: a tile's trailing blocks past the context are never
+    # read, whatever their table entries hold (a NaN block, -1, an id past the pool)
+    cfg = workloads.Config("smallblk", "bf16", 7, 16, 4, 128, B, ("uniform", 1, 90), seed=300 + B)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    for P in (0, 3 * B):
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P, do_copy=False, do_write=False)
+        clean = H.bits(d["out"]).copy()
+        attended = set(np.concatenate([step.block_tables[s, :-(-int(c) // B)]
+                                       for s, c in enumerate(step.context_lens)]).tolist())
+        poison = [b for b in range(wl.num_blocks) if b not in attended][0]
+        kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+        wl.k_cache[poison] = np.uint16(0x7FC1)
+        wl.v_cache[poison] = np.uint16(0x7FC1)
+        for pad in (poison, -1, wl.num_blocks + 7):
+            tables = step.block_tables.copy()
+            for s, c in enumerate(step.context_lens.tolist()):
+                tables[s, -(-c // B):] = pad
+            st2 = pbatch.DecodeStep(**{**step.__dict__, "block_tables": tables})
+            _say("small-block padding", B, "P", P, "pad", pad)
+            d2 = H.upload(wl, st2)
+            H.gpu_step(wl, st2, d2, P, do_copy=False, do_write=False)
+            assert H.bits(d2["out"]).tobytes() == clean.tobytes()
+        wl.k_cache[:], wl.v_cache[:] = kc, vc
 
 
 def test_split_matches_unsplit_within_tolerance():
