@@ -176,3 +176,56 @@ def dense_attention(q, k_cache, v_cache, block_tables, context_lens, scale: floa
             w = np.exp(x - x.max())
             out[s, h] = (w @ V[:, h // g, :]) / w.sum()
     return out
+
+
+# ---------------------------------------------------------------------------
+# the head-major cache layout (page "PagedAttention", PidokuInfra topic 10, section 5,
+# "The layout, more precisely"): per block, per KV head,
+#   key_cache   [num_blocks, num_kv_heads, head_dim / x, block_size, x],  x = 16 / sizeof(dtype)
+#   value_cache [num_blocks, num_kv_heads, head_dim, block_size]
+# so that 16 bytes of K hold x consecutive head dims of one token and the block_size tokens
+# of one V head dim are consecutive.  The values are those of the row layout
+# [num_blocks, block_size, num_kv_heads, head_dim], only placed differently.
+# ---------------------------------------------------------------------------
+
+def head_major_x(dtype) -> int:
+    """Elements of one 16-byte K vector: 8 for bf16, 4 for fp32."""
+    return 16 // np.dtype(dtype).itemsize
+
+
+def rows_from_head_major(k_hm: np.ndarray, v_hm: np.ndarray):
+    """Row-layout copies: K[b, o, h, d] = K_hm[b, h, d // x, o, d % x], V[b, o, h, d] = V_hm[b, h, d, o]."""
+    N, Hkv, Dx, B, x = k_hm.shape
+    k = np.ascontiguousarray(k_hm.transpose(0, 3, 1, 2, 4).reshape(N, B, Hkv, Dx * x))
+    v = np.ascontiguousarray(v_hm.transpose(0, 3, 1, 2))
+    return k, v
+
+
+def head_major_from_rows(k_rows: np.ndarray, v_rows: np.ndarray):
+    """The head-major placement of row-layout K/V [N, B, Hkv, D]."""
+    N, B, Hkv, D = k_rows.shape
+    x = head_major_x(k_rows.dtype)
+    k = np.ascontiguousarray(k_rows.reshape(N, B, Hkv, D // x, x).transpose(0, 2, 3, 1, 4))
+    v = np.ascontiguousarray(v_rows.transpose(0, 2, 3, 1))
+    return k, v
+
+
+def kv_write_head_major(k_new, v_new, k_hm, v_hm, slots) -> None:
+    """In place: token i with slot s = b * B + o lands in K_hm[b, :, :, o, :] and V_hm[b, :, :, o]."""
+    N, Hkv, Dx, B, x = k_hm.shape
+    sl = np.asarray(slots, dtype=np.int64)
+    if len(set(sl.tolist())) != len(sl):
+        raise OracleError(_ERRORS[-3])
+    for i, s in enumerate(sl.tolist()):
+        if s < 0 or s >= N * B:
+            raise OracleError(_ERRORS[-2])
+        b, o = divmod(s, B)
+        k_hm[b, :, :, o, :] = k_new[i].reshape(Hkv, Dx, x)
+        v_hm[b, :, :, o] = v_new[i]
+
+
+def attention_head_major(q, k_hm, v_hm, block_tables, context_lens, scale: float, partition_size: int = 0,
+                         items=None, num_threads: int = 0) -> np.ndarray:
+    """fp64 paged attention on a head-major pool: the same attention as on the row layout."""
+    k, v = rows_from_head_major(k_hm, v_hm)
+    return attention(q, k, v, block_tables, context_lens, scale, partition_size, items, num_threads)

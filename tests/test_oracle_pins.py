@@ -443,3 +443,59 @@ def test_attention_rejects_bad_inputs():
         oracle.attention(np.ascontiguousarray(q[:, :3]), kc, vc, bt, ctx, 0.25)                          # 3 % 2 != 0
     with pytest.raises(oracle.OracleError):
         oracle.attention(q, kc, vc, bt, ctx, 0.25, partition_size=6)               # not a multiple of B
+
+
+# ---------------------------------------------------------------------------
+# head-major cache layout (PidokuInfra page, section 5 "The layout, more precisely")
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,B", [("bf16", 16), ("bf16", 8), ("f32", 4), ("f32", 32)])
+def test_head_major_layout_byte_properties(dt, B):
+    # the page prints key_cache [N, Hkv, D/x, B, x] with x = 16 / sizeof(dtype), so 16 bytes
+    # of K are x consecutive head dims of one token, and value_cache [N, Hkv, D, B], so the
+    # B tokens of one head dim of V are consecutive; checked on the raw bytes
+    N, Hkv, D = 5, 3, 32
+    e = 2 if dt == "bf16" else 4
+    x = 16 // e
+    k = workloads.normal(N * B * Hkv * D, 7, 1, dt).reshape(N, B, Hkv, D)
+    v = workloads.normal(N * B * Hkv * D, 7, 2, dt).reshape(N, B, Hkv, D)
+    khm, vhm = oracle.head_major_from_rows(k, v)
+    assert oracle.head_major_x(k.dtype) == x
+    assert khm.shape == (N, Hkv, D // x, B, x) and vhm.shape == (N, Hkv, D, B)
+    kb, vb = khm.tobytes(), vhm.tobytes()
+    rng = np.random.default_rng(B)
+    for _ in range(200):
+        b, o, h, d = (int(rng.integers(n)) for n in (N, B, Hkv, D))
+        j = d // x
+        off = (((b * Hkv + h) * (D // x) + j) * B + o) * 16
+        assert kb[off:off + 16] == k[b, o, h, j * x:(j + 1) * x].tobytes()
+        off = ((b * Hkv + h) * D + d) * B * e
+        assert vb[off:off + B * e] == np.ascontiguousarray(v[b, :, h, d]).tobytes()
+    k2, v2 = oracle.rows_from_head_major(khm, vhm)
+    assert k2.tobytes() == k.tobytes() and v2.tobytes() == v.tobytes()
+
+
+def test_kv_write_head_major_matches_row_write():
+    N, B, Hkv, D, T = 9, 16, 2, 64, 5
+    k = _special_rows(N * B, Hkv * D, 11).reshape(N, B, Hkv, D).copy()
+    v = _special_rows(N * B, Hkv * D, 12).reshape(N, B, Hkv, D).copy()
+    kn = _special_rows(T, Hkv * D, 13).reshape(T, Hkv, D)
+    vn = _special_rows(T, Hkv * D, 14).reshape(T, Hkv, D)
+    slots = [0, 17, 143, 70, 31]
+    khm, vhm = oracle.head_major_from_rows(k, v)
+    oracle.kv_write(kn, vn, k, v, slots)
+    oracle.kv_write_head_major(kn, vn, khm, vhm, slots)
+    k2, v2 = oracle.head_major_from_rows(k, v)
+    assert khm.tobytes() == k2.tobytes() and vhm.tobytes() == v2.tobytes()
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write_head_major(kn[:2], vn[:2], khm, vhm, [3, 3])
+    with pytest.raises(oracle.OracleError):
+        oracle.kv_write_head_major(kn[:1], vn[:1], khm, vhm, [N * B])
+
+
+def test_attention_head_major_is_row_attention():
+    q, kc, vc, bt, ctx, m, _ = _small(5, 3, 8, 2, 32, 8, 60, "bf16")
+    khm, vhm = oracle.head_major_from_rows(kc, vc)
+    o = oracle.attention(q, kc, vc, bt, ctx, 0.25, 16)
+    o2 = oracle.attention_head_major(q, khm, vhm, bt, ctx, 0.25, 16)
+    assert o.tobytes() == o2.tobytes()
