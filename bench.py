@@ -107,6 +107,13 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     ctx = batch.to_torch(step.context_lens, dev)
     slots = batch.to_torch(step.slot_mapping, dev)
     pairs = batch.to_torch(step.copy_pairs, dev)
+    hm = layout == "head_major"
+    if hm:
+        # the same values placed head-major: k [N, Hkv, D/x, B, x], v [N, Hkv, D, B]
+        kc, vc = batch.to_head_major(kc, vc)
+    write = binding.paged_kv_write_head_major if hm else binding.paged_kv_write
+    copy = binding.copy_blocks_head_major if hm else binding.copy_blocks
+    attend = binding.paged_attention_decode_head_major if hm else binding.paged_attention_decode
     out = torch.empty_like(q)
     ws_bytes = binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim, step.max_context_len,
                                                 partition)
@@ -119,11 +126,11 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
 
     def one_step(i=None):
         if n_pairs:
-            binding.copy_blocks(kc, vc, pairs)
-        binding.paged_kv_write(kn, vn, kc, vc, slots)
+            copy(kc, vc, pairs)
+        write(kn, vn, kc, vc, slots)
         if i is not None:
             ev[i][0].record()
-        binding.paged_attention_decode(out, q, kc, vc, tables, ctx, step.max_context_len, wl.scale, partition, ws)
+        attend(out, q, kc, vc, tables, ctx, step.max_context_len, wl.scale, partition, ws)
         if i is not None:
             ev[i][1].record()
 
@@ -231,8 +238,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
-    ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous"],
-                    help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool")
+    ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous", "head_major"],
+                    help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool; "
+                         "head_major: the shuffled pool in the head-major cache layout")
     ap.add_argument("--block-size", type=int, default=None,
                     help="run the workload with this block size instead of its configured one")
     ap.add_argument("--sweep-block-size", action="store_true",

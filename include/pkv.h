@@ -145,6 +145,43 @@ pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mappin
                        int32_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                        pkv_dtype dtype, void *stream);
 
+/*
+ * The head-major cache layout (PidokuInfra page, section 5 "The layout, more precisely"):
+ *   k_cache : [num_blocks, num_kv_heads, head_dim / x, block_size, x],  x = 16 / elem_bytes
+ *   v_cache : [num_blocks, num_kv_heads, head_dim, block_size]
+ * The same values as the row layout, placed so that one (block, KV head) is contiguous:
+ * K[b, o, h, d] of the row layout is k_cache[b, h, d / x, o, d % x] here and V[b, o, h, d]
+ * is v_cache[b, h, d, o].  A block is still num_kv_heads * head_dim * block_size elements,
+ * so copy_blocks serves both layouts unchanged.
+ *
+ * paged_kv_write_head_major -- paged_kv_write into this layout: token i with slot
+ * s = b * block_size + o fills k_cache[b, :, :, o, :] and v_cache[b, :, :, o] from
+ * k_new[i], v_new[i] ([T, num_kv_heads, head_dim]); arguments, checks and device-value
+ * handling as for paged_kv_write.
+ */
+pkv_status paged_kv_write_head_major(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                     const int64_t *slot_mapping, int64_t num_tokens, int32_t num_blocks,
+                                     int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pkv_dtype dtype,
+                                     void *stream);
+
+/*
+ * paged_attention_decode_head_major -- paged_attention_decode on head-major caches: the same
+ * arguments, workspace, checks and results (the same attention; outputs may differ from the
+ * row layout's only in rounding).  Built for bf16, head_dim 128, block_size in
+ * {16, 32, 64, 128}, num_heads / num_kv_heads <= 16 (PKV_ERR_UNSUPPORTED otherwise;
+ * pkv_attention_path_head_major reports it).
+ */
+pkv_status paged_attention_decode_head_major(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_blocks, float scale,
+                                             int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                             pkv_dtype dtype, void *stream);
+
+pkv_path pkv_attention_path_head_major(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, pkv_dtype dtype);
+
 /* Static, human-readable name of a status code. */
 const char *pkv_status_string(pkv_status status);
 

@@ -119,6 +119,16 @@ def from_torch_bits(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def to_head_major(k_cache, v_cache):
+    """Row-layout device caches [N, B, Hkv, D] placed in the head-major layout:
+    k [N, Hkv, D/x, B, x] with x = 16 / element bytes, v [N, Hkv, D, B] (the same values)."""
+    N, B, Hkv, D = k_cache.shape
+    x = 16 // k_cache.element_size()
+    k = k_cache.reshape(N, B, Hkv, D // x, x).permute(0, 2, 3, 1, 4).contiguous()
+    v = v_cache.permute(0, 2, 3, 1).contiguous()
+    return k, v
+
+
 def step_for(wl, which: str = "steady") -> DecodeStep:
     """The decode step of a synthetic workload ('steady' or 'fork' for the fork workload)."""
     cfg = wl.cfg

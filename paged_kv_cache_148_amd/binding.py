@@ -19,7 +19,8 @@ PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA = 0, 1, 2
 
 # every symbol include/pkv.h declares
 EXPORTS = ("paged_kv_write", "paged_attention_decode", "copy_blocks", "pkv_attention_workspace_size",
-           "pkv_attention_path", "pkv_status_string")
+           "pkv_attention_path", "pkv_status_string", "paged_kv_write_head_major",
+           "paged_attention_decode_head_major", "pkv_attention_path_head_major")
 
 _lib = None
 
@@ -53,6 +54,12 @@ def lib():
         L.paged_attention_decode.restype = ctypes.c_int
         L.paged_attention_decode.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.c_float, i32, p, sz, ctypes.c_int, p]
+        L.paged_kv_write_head_major.restype = ctypes.c_int
+        L.paged_kv_write_head_major.argtypes = [p, p, p, p, p, i64, i32, i32, i32, i32, ctypes.c_int, p]
+        L.paged_attention_decode_head_major.restype = ctypes.c_int
+        L.paged_attention_decode_head_major.argtypes = L.paged_attention_decode.argtypes
+        L.pkv_attention_path_head_major.restype = ctypes.c_int
+        L.pkv_attention_path_head_major.argtypes = [i32, i32, i32, i32, ctypes.c_int]
         L.copy_blocks.restype = ctypes.c_int
         L.copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i32, ctypes.c_int, p]
         L.pkv_status_string.restype = ctypes.c_char_p
@@ -162,3 +169,73 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q, stream))
     _check(st, "paged_attention_decode")
+
+
+# ---------------------------------------------------------------------------
+# head-major cache layout: k_cache [N, Hkv, D/x, B, x] (x = 16 / element bytes),
+# v_cache [N, Hkv, D, B]
+# ---------------------------------------------------------------------------
+
+def _head_major_shape(k_cache, v_cache):
+    N, Hkv, Dx, B, x = k_cache.shape
+    D = Dx * x
+    if x * k_cache.element_size() != 16 or tuple(v_cache.shape) != (N, Hkv, D, B):
+        raise ValueError("head-major caches must be k [N, Hkv, D/x, B, x] with x * elem = 16 and v [N, Hkv, D, B]")
+    return N, B, Hkv, D
+
+
+def attention_path_head_major(num_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                              dtype_code: int) -> int:
+    return int(lib().pkv_attention_path_head_major(num_heads, num_kv_heads, head_dim, block_size, dtype_code))
+
+
+def paged_kv_write_head_major(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """paged_kv_write into head-major caches."""
+    torch = _torch()
+    N, B, Hkv, D = _head_major_shape(k_cache, v_cache)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new/v_new must be [T, Hkv, D]")
+    dt = k_cache.dtype
+    st = lib().paged_kv_write_head_major(
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(slot_mapping, "slot_mapping", torch.int64), T, N, B, Hkv, D, _dtype_code(k_cache),
+        _stream(k_cache, stream))
+    _check(st, "paged_kv_write_head_major")
+
+
+def copy_blocks_head_major(k_cache, v_cache, block_mapping, stream=None) -> None:
+    """copy_blocks on head-major caches (a block is the same bytes in either layout)."""
+    torch = _torch()
+    N, B, Hkv, D = _head_major_shape(k_cache, v_cache)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [P, 2]")
+    dt = k_cache.dtype
+    st = lib().copy_blocks(_dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+                           _dev(block_mapping, "block_mapping", torch.int64), block_mapping.shape[0],
+                           N, B, Hkv, D, _dtype_code(k_cache), _stream(k_cache, stream))
+    _check(st, "copy_blocks")
+
+
+def paged_attention_decode_head_major(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                                      scale: float, partition_size: int = 0, workspace=None, stream=None) -> None:
+    """paged_attention_decode on head-major caches."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, B, Hkv, D2 = _head_major_shape(k_cache, v_cache)
+    if D2 != D or tuple(out.shape) != (S, Hq, D):
+        raise ValueError("shape mismatch between q/out [S, Hq, D] and the caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if workspace is None:
+        need = attention_workspace_size(S, Hq, D, max_context_len, partition_size)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr())
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dt = q.dtype
+    st = lib().paged_attention_decode_head_major(
+        _dev(out, "out", dt), _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q, stream))
+    _check(st, "paged_attention_decode_head_major")

@@ -576,8 +576,17 @@ __device__ __forceinline__ void mfma_finish(const AttnArgs &a, const MItem &it, 
   }
 }
 
-template <int B, int NB>
+// HM: the head-major cache layout (K [N, Hkv, D/8, B, 8], V [N, Hkv, D, B]; page
+// "PagedAttention", PidokuInfra topic 10, section 5 "The layout, more precisely").  One
+// (block, KV head) is then a contiguous 4 KB (B = 16) of K and of V.  Lane (c16, grp) reads
+// K chunk 4c + grp of token c16 straight into the QK A operand (instruction c: 16 tokens x
+// 4 chunks, 1 KB contiguous at B = 16) and, for P.V MFMA i, the 4 tokens 4grp .. of head dim
+// 16i + c16 (8 bytes; instruction i: 16 dims x 16 tokens, 512 B contiguous at B = 16) straight
+// into its A operand: no LDS staging and no byte permutes.  The accumulator of MFMA i then
+// holds dims 16i + 4grp + r.  Blocks of 16 slots or more.
+template <int B, int NB, bool HM>
 __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
+  static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
   constexpr int D = 128;
   __shared__ MfmaSmem sm;
   extern __shared__ int sm_dyn[];
@@ -630,9 +639,24 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     int bad_cur = 0, bad_next = 0;
 
     // Loads of tile i of an item (zero-range descriptors past its live tiles).
-    auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd) {
+    auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const bool live = i < it.n_my;
       const int tok0 = (it.tile_lo + wave + kWaves * i) << 4;
+      if constexpr (HM) {
+        constexpr uint32_t hb_bytes = D * B * 2;   // one (block, KV head) of K or of V
+        const size_t off = ((size_t)phys[0] * a.Hkv + it.kvh) * hb_bytes;
+        const uint32_t range = live ? hb_bytes : 0u;
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kpool + off, range);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vpool + off, range);
+        const int t0b = tok0 % B;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          kd[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, (grp * B + c16) * 16, (4 * c * B + t0b) * 16, kNontemporal);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          vd2[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (c16 * B + 4 * grp) * 2, (16 * j * B + t0b) * 2, kNontemporal);
+        return;
+      }
       __amdgpu_buffer_rsrc_t rk[BPT], rv[BPT];
 #pragma unroll
       for (int h = 0; h < BPT; ++h) {
@@ -654,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
     };
     // tile i of the current item
-    auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd) {
+    auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const bool live = i < cur.n_my;
       if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
 #pragma unroll
@@ -671,10 +695,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
           phys[h] = 0;
         }
       }
-      load_tile(cur, i, phys, kd, vd);
+      load_tile(cur, i, phys, kd, vd, vd2);
     };
     // tile i (< NB - 1) of the next item
-    auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd) {
+    auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const int tok0 = (nxt.tile_lo + wave + kWaves * i) << 4;
       int phys[BPT];
 #pragma unroll
@@ -685,7 +709,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
           phys[h] = 0;
         }
       }
-      load_tile(nxt, i, phys, kd, vd);
+      load_tile(nxt, i, phys, kd, vd, vd2);
     };
 
     float m = kNegInf, lsum = 0.f;
@@ -693,20 +717,25 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int i, u32x4 *kr, u32x4 *vr) {
+    auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
       const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
-      // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t sits
-      // at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token, 16
-      // chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of 64
-      // banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * grp + r;
-        kst[t * 16 + (c16 ^ t)] = kr[r];
-      }
       u32x4 kop[4];
+      if constexpr (HM) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
+        for (int c = 0; c < 4; ++c) kop[c] = kr[c];   // loaded in the A layout
+      } else {
+        // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t
+        // sits at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token,
+        // 16 chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of
+        // 64 banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * grp + r;
+          kst[t * 16 + (c16 ^ t)] = kr[r];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
+      }
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -715,13 +744,25 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 
       // scores of tile rows 4grp + r for head c16; positions outside [t0, t1) are masked
       float sv[4], mx = kNegInf;
+      uint32_t keep01 = 0u, keep23 = 0u;   // head-major V: halves of the tokens in range
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tk = tok0 + (r / RPI) * B + RPI * grp + r % RPI;
         const bool ok = tk >= cur.t0 && tk < cur.t1;
         sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
-        if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
+        if constexpr (HM) {
+          const uint32_t half = ok ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
+          if (r < 2) keep01 |= half; else keep23 |= half;
+        } else {
+          if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
+        }
         mx = fmaxf(mx, sv[r]);
+      }
+      if constexpr (HM) {
+        if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -744,6 +785,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        if constexpr (HM) {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vr2[j]), pop, acc[j], 0, 0, 0);
+          continue;
+        }
         const int wd = j >> 1;
         uint32_t a01, a23;
         if (j & 1) {
@@ -760,8 +805,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 
     // the stream's first tiles
     u32x4 kbuf[NB][4], vbuf[NB][4];
+    u32x2 vbuf2[NB][HM ? 8 : 1];   // head-major V pieces (unused on the row layout)
 #pragma unroll
-    for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j]);
+    for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
 
     for (int k = 0;; ++k) {
       // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
@@ -781,9 +827,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       auto body = [&](int x) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-          issue_cur(x + j + NB - 1, kbuf[(j + NB - 1) % NB], vbuf[(j + NB - 1) % NB]);
+          issue_cur(x + j + NB - 1, kbuf[(j + NB - 1) % NB], vbuf[(j + NB - 1) % NB], vbuf2[(j + NB - 1) % NB]);
           __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
-          if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j]);
+          if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
         }
       };
       int x = 0;
@@ -800,11 +846,11 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (j == 0)
-          issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1]);
+          issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1], vbuf2[NB - 1]);
         else
-          issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1]);
+          issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1], vbuf2[j - 1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j]);
+        if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
       }
 
       // merge the waves' states of it_k (the next item's first loads are in flight)
@@ -816,7 +862,10 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         sm.l[mb][c16][wave] = lh;
       }
       if (lane == 0) sm.bad[mb][wave] = bad_cur;
-      {
+      if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][c16][16 * i + 4 * grp]) = acc[i];
+      } else {              // MFMA i holds dims 32grp + 8r + i
         float *dst = &sm.o[mb][wave][c16][32 * grp];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1153,6 +1202,13 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   return B <= 32 && vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
 }
 
+// Head-major layout: the MFMA kernel only (bf16, D = 128, blocks of 16 slots or more).
+static pkv_path select_path_head_major(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PKV_PATH_NONE;
+  if (dt != PKV_DTYPE_BF16 || D != 128 || Hq / Hkv > 16) return PKV_PATH_NONE;
+  return B == 16 || B == 32 || B == 64 || B == 128 ? PKV_PATH_MFMA : PKV_PATH_NONE;
+}
+
 typedef void (*Pass1Fn)(AttnArgs);
 
 template <typename T, int D, int G>
@@ -1175,15 +1231,23 @@ static Pass1Fn vec_fn(int g, int B) {
   }
 }
 
-static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g) {
+static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major) {
+  if (head_major) {
+    switch (B) {
+      case 16: return attn_mfma_kernel<16, kMfmaDepth, true>;
+      case 32: return attn_mfma_kernel<32, kMfmaDepth, true>;
+      case 64: return attn_mfma_kernel<64, kMfmaDepth, true>;
+      default: return attn_mfma_kernel<128, kMfmaDepth, true>;
+    }
+  }
   if (path == PKV_PATH_MFMA) {
     switch (B) {
-      case 4: return attn_mfma_kernel<4, kMfmaDepth>;
-      case 8: return attn_mfma_kernel<8, kMfmaDepth>;
-      case 16: return attn_mfma_kernel<16, kMfmaDepth>;
-      case 32: return attn_mfma_kernel<32, kMfmaDepth>;
-      case 64: return attn_mfma_kernel<64, kMfmaDepth>;
-      default: return attn_mfma_kernel<128, kMfmaDepth>;
+      case 4: return attn_mfma_kernel<4, kMfmaDepth, false>;
+      case 8: return attn_mfma_kernel<8, kMfmaDepth, false>;
+      case 16: return attn_mfma_kernel<16, kMfmaDepth, false>;
+      case 32: return attn_mfma_kernel<32, kMfmaDepth, false>;
+      case 64: return attn_mfma_kernel<64, kMfmaDepth, false>;
+      default: return attn_mfma_kernel<128, kMfmaDepth, false>;
     }
   }
   if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
@@ -1229,19 +1293,19 @@ extern "C" size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_hea
   return kQueueBytes + (size_t)num_seqs * num_heads * np * (head_dim + 32) * sizeof(float);
 }
 
-extern "C" pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
-                                             const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                             const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
-                                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                                             int32_t block_size, int32_t num_blocks, float scale,
-                                             int32_t partition_size, void *workspace, size_t workspace_bytes,
-                                             pkv_dtype dtype, void *stream) {
+// Both cache layouts: the row layout [N, B, Hkv, D] and the head-major layout.
+static pkv_status decode(bool head_major, void *out, const void *q, const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
+                         int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
+                         void *workspace, size_t workspace_bytes, pkv_dtype dtype, void *stream) {
   if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1 || max_context_len < 1 || partition_size < 0)
     return PKV_ERR_INVALID_ARG;
   if (num_heads % num_kv_heads != 0) return PKV_ERR_INVALID_ARG;
-  const pkv_path path = select_path(num_heads, num_kv_heads, head_dim, block_size, dtype);
+  const pkv_path path = head_major ? select_path_head_major(num_heads, num_kv_heads, head_dim, block_size, dtype)
+                                   : select_path(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (path == PKV_PATH_NONE) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_INVALID_ARG;
   if (partition_size > 0 && partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
@@ -1287,7 +1351,7 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const bool bf16 = dtype == PKV_DTYPE_BF16;
-  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g);
+  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major);
   // persistent workgroups when the schedule fits in LDS, else one workgroup per possible item
   size_t dyn_lds = 0;
   int64_t grid = items;
@@ -1319,4 +1383,31 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+extern "C" pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                             const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                             const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t num_blocks, float scale,
+                                             int32_t partition_size, void *workspace, size_t workspace_bytes,
+                                             pkv_dtype dtype, void *stream) {
+  return decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, workspace,
+                workspace_bytes, dtype, stream);
+}
+
+extern "C" pkv_status paged_attention_decode_head_major(
+    void *out, const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,
+    int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+    int32_t partition_size, void *workspace, size_t workspace_bytes, pkv_dtype dtype, void *stream) {
+  return decode(true, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, workspace,
+                workspace_bytes, dtype, stream);
+}
+
+extern "C" pkv_path pkv_attention_path_head_major(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t block_size, pkv_dtype dtype) {
+  return select_path_head_major(num_heads, num_kv_heads, head_dim, block_size, dtype);
 }

@@ -35,6 +35,35 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const u32x4 *__restrict__
   }
 }
 
+// The same write into the head-major layout (page "PagedAttention", PidokuInfra topic 10,
+// section 5 "The layout, more precisely"): K [N, Hkv, D/x, B, x] with x = 16 / elem_bytes,
+// V [N, Hkv, D, B].  Slot s = b * B + o: K vector j (x head dims) of head h goes to 16-byte
+// vector ((b * Hkv + h) * (D/x) + j) * B + o; V element (h, d) to element
+// ((b * Hkv + h) * D + d) * B + o.  One workgroup per token.
+template <typename E>
+__global__ __launch_bounds__(256) void kv_write_head_major_kernel(const u32x4 *__restrict__ k_new,
+                                                                  const E *__restrict__ v_new,
+                                                                  u32x4 *__restrict__ k_cache, E *__restrict__ v_cache,
+                                                                  const int64_t *__restrict__ slots, int64_t num_tokens,
+                                                                  int num_kv_heads, int head_dim, int block_size,
+                                                                  int64_t num_slots) {
+  const int kvec = head_dim * (int)sizeof(E) / 16;   // K vectors per head
+  const int row_k = num_kv_heads * kvec, row_v = num_kv_heads * head_dim;
+  for (int64_t tok = blockIdx.x; tok < num_tokens; tok += gridDim.x) {
+    const int64_t slot = slots[tok];
+    if (slot < 0 || slot >= num_slots) continue;  // -1 / out of range: no write
+    const int64_t b = slot / block_size, o = slot % block_size;
+    for (int c = threadIdx.x; c < row_k; c += blockDim.x) {
+      const int64_t hj = b * row_k + c;   // (b * Hkv + h) * kvec + j
+      k_cache[hj * block_size + o] = k_new[tok * row_k + c];
+    }
+    for (int c = threadIdx.x; c < row_v; c += blockDim.x) {
+      const int64_t hd = b * row_v + c;   // (b * Hkv + h) * D + d
+      v_cache[hd * block_size + o] = v_new[tok * row_v + c];
+    }
+  }
+}
+
 // grid = (pairs, chunks of one block, 2 tensors).  Each workgroup copies up to
 // 256 threads x 4 vectors = 16 KiB of one block of one tensor.
 constexpr int kCopyVecsPerThread = 4;
@@ -98,6 +127,33 @@ extern "C" pkv_status paged_kv_write(const void *k_new, const void *v_new, void 
   hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream,
                      (const u32x4 *)k_new, (const u32x4 *)v_new, (u32x4 *)k_cache, (u32x4 *)v_cache, slot_mapping,
                      num_tokens, row_vecs, (int64_t)num_blocks * block_size);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" pkv_status paged_kv_write_head_major(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                                const int64_t *slot_mapping, int64_t num_tokens, int32_t num_blocks,
+                                                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                                pkv_dtype dtype, void *stream) {
+  if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (!shape_ok(block_size, num_kv_heads, head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t grid = num_tokens < 65535 ? num_tokens : 65535;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == PKV_DTYPE_BF16)
+    hipLaunchKernelGGL(kv_write_head_major_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, st,
+                       (const u32x4 *)k_new, (const uint16_t *)v_new, (u32x4 *)k_cache, (uint16_t *)v_cache,
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_slots);
+  else
+    hipLaunchKernelGGL(kv_write_head_major_kernel<uint32_t>, dim3((unsigned)grid), dim3(256), 0, st,
+                       (const u32x4 *)k_new, (const uint32_t *)v_new, (u32x4 *)k_cache, (uint32_t *)v_cache,
+                       slot_mapping, num_tokens, num_kv_heads, head_dim, block_size, num_slots);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

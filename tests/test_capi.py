@@ -51,6 +51,15 @@ def test_workspace_size(L):
     assert binding.attention_workspace_size(2, 4, 64, 513, 512) == 256 + 2 * 4 * 2 * 96 * 4
 
 
+def test_path_selection_head_major(L):
+    assert binding.attention_path_head_major(64, 8, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA
+    assert binding.attention_path_head_major(32, 32, 128, 128, PKV_DTYPE_BF16) == PKV_PATH_MFMA
+    assert binding.attention_path_head_major(32, 8, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE    # below a tile
+    assert binding.attention_path_head_major(8, 8, 128, 16, PKV_DTYPE_F32) == PKV_PATH_NONE     # bf16 only
+    assert binding.attention_path_head_major(8, 8, 64, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE
+    assert binding.attention_path_head_major(64, 2, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE   # g = 32
+
+
 def test_path_selection(L):
     assert binding.attention_path(64, 8, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA
     assert binding.attention_path(32, 8, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA

@@ -335,6 +335,119 @@ def test_small_blocks_padding_never_read(B):
         wl.k_cache[:], wl.v_cache[:] = kc, vc
 
 
+# ---------------------------------------------------------------------------
+# head-major cache layout
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,B", [("bf16", 16), ("bf16", 128), ("f32", 32)])
+def test_head_major_write_and_copy_bit_exact(dt, B):
+    cfg = workloads.Config("hm", dt, 6, 16, 4, 128, B, ("uniform", 1, 3 * B), seed=400 + B)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])
+    _say("head-major write", dt, B)
+    binding.paged_kv_write_head_major(d["k_new"], d["v_new"], khm, vhm, d["slot_mapping"])
+    o = H.oracle_step(wl, "steady", attend=False)[0]
+    rk, rv = oracle.head_major_from_rows(wl.k_cache, wl.v_cache)
+    oracle.kv_write_head_major(wl.k_new, wl.v_new, rk, rv, o["slot_mapping"])
+    import torch
+    torch.cuda.synchronize()
+    assert H.bits(khm).tobytes() == rk.tobytes() and H.bits(vhm).tobytes() == rv.tobytes()
+    rng = np.random.default_rng(B)
+    perm = rng.permutation(wl.num_blocks)
+    npairs = wl.num_blocks // 2
+    pairs = np.stack([perm[:npairs], perm[npairs:2 * npairs]], axis=1).astype(np.int64)
+    _say("head-major copy", dt, B, pairs.shape)
+    binding.copy_blocks_head_major(khm, vhm, pbatch.to_torch(pairs, "cuda"))
+    torch.cuda.synchronize()
+    oracle.copy_blocks(rk.reshape(rk.shape[0], -1, 1, 1), rv.reshape(rv.shape[0], -1, 1, 1), pairs)
+    assert H.bits(khm).tobytes() == rk.tobytes() and H.bits(vhm).tobytes() == rv.tobytes()
+
+
+HM_SHAPES = [
+    # S, Hq, Hkv, B, ctx range, partition sizes
+    (5, 16, 2, 16, (1, 700), (0, 64)),      # g = 8
+    (4, 8, 8, 16, (1, 600), (0, 128)),      # g = 1
+    (4, 24, 8, 32, (1, 500), (0, 96)),      # g = 3, B = 32
+    (3, 16, 4, 128, (1, 1500), (0, 256)),   # g = 4, B = 128
+    (3, 8, 2, 64, (4200, 9000), (0, 512)),  # more than 64 tiles per wave
+]
+
+
+@pytest.mark.parametrize("shape", HM_SHAPES, ids=[f"g{s[1]//s[2]}-B{s[3]}" for s in HM_SHAPES])
+def test_head_major_attention_parity(shape):
+    S, Hq, Hkv, B, (lo, hi), parts = shape
+    cfg = workloads.Config("hm", "bf16", S, Hq, Hkv, 128, B, ("uniform", lo, hi), seed=500 + Hq + B)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    for P in parts:
+        _say("head-major attention", shape, "P", P)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P, do_attn=False)        # copies and write on the row layout ...
+        khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])   # ... then placed head-major
+        binding.paged_attention_decode_head_major(d["out"], d["q"], khm, vhm, d["block_tables"],
+                                                  d["context_lens"], step.max_context_len, wl.scale, P)
+        o, kc, vc, _ = H.oracle_step(wl, "steady", P, attend=False)
+        rk, rv = oracle.head_major_from_rows(kc, vc)
+        ref = oracle.attention_head_major(wl.q, rk, rv, o["block_tables"], o["context_lens"], wl.scale, P)
+        H.check_close(H.bits(d["out"]), ref, "bf16", f"head-major {shape} P={P}")
+
+
+def test_head_major_unread_slots_and_padding_never_read():
+    cfg = workloads.Config("hm", "bf16", 6, 32, 4, 128, 16, ("uniform", 1, 200), seed=611)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    import torch
+    for P in (0, 48):
+        d = H.upload(wl, step)
+        khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])
+        binding.paged_attention_decode_head_major(d["out"], d["q"], khm, vhm, d["block_tables"],
+                                                  d["context_lens"], step.max_context_len, wl.scale, P)
+        clean = H.bits(d["out"]).copy()
+        B = cfg.block_size
+        attended = set(np.concatenate([step.block_tables[s, :-(-int(c) // B)]
+                                       for s, c in enumerate(step.context_lens)]).tolist())
+        poison = [b for b in range(wl.num_blocks) if b not in attended][0]
+        kp, vp = wl.k_cache.copy(), wl.v_cache.copy()
+        kp[poison] = np.uint16(0x7FC1)
+        vp[poison] = np.uint16(0x7FC1)
+        tables = step.block_tables.copy()
+        for s, c in enumerate(step.context_lens.tolist()):
+            nb = -(-c // B)
+            last = tables[s, nb - 1]
+            kp[last, c - (nb - 1) * B:] = np.uint16(0x7FC1)
+            vp[last, c - (nb - 1) * B:] = np.uint16(0x7FC1)
+            tables[s, nb:] = poison
+        _say("head-major poison", P)
+        khm, vhm = pbatch.to_head_major(pbatch.to_torch(kp, "cuda", True), pbatch.to_torch(vp, "cuda", True))
+        tb = pbatch.to_torch(tables, "cuda")
+        binding.paged_attention_decode_head_major(d["out"], d["q"], khm, vhm, tb, d["context_lens"],
+                                                  step.max_context_len, wl.scale, P)
+        torch.cuda.synchronize()
+        assert H.bits(d["out"]).tobytes() == clean.tobytes()
+
+
+def test_head_major_full_size_sampled_parity():
+    wl = _wl("gqa70b")
+    step = pbatch.step_for(wl)
+    cfg = wl.cfg
+    rng = np.random.default_rng(13)
+    items = np.unique(rng.integers(0, cfg.num_seqs * cfg.num_heads, size=96))
+    for P in (0, 2048):
+        _say("head-major gqa70b sampled", "P", P)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P, do_attn=False)
+        khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])
+        binding.paged_attention_decode_head_major(d["out"], d["q"], khm, vhm, d["block_tables"],
+                                                  d["context_lens"], step.max_context_len, wl.scale, P)
+        o, kc, vc, _ = H.oracle_step(wl, "steady", P, attend=False)
+        ref = oracle.attention(wl.q, kc, vc, o["block_tables"], o["context_lens"], wl.scale, P, items)
+        got = H.bits(d["out"]).reshape(cfg.num_seqs * cfg.num_heads, -1)[items]
+        H.check_close(got, ref, "bf16", f"head-major gqa70b P={P}")
+        del khm, vhm
+
+
 def test_split_matches_unsplit_within_tolerance():
     wl = _wl("gqa70b", num_seqs=10)
     step = pbatch.step_for(wl)
