@@ -119,3 +119,42 @@ def build_tables(seqs, max_blocks: int | None = None, pad: int = 0):
     for i, s in enumerate(seqs):
         out[i, :len(s["table"])] = s["table"]
     return out
+
+
+class PrefixModel:
+    """Prefix reuse of full prompt blocks, as a plain model (test infrastructure): a new
+    prompt's leading blocks are reused when its first j * B tokens equal those of a block
+    held in the map (PidokuInfra page, section 5 "The relationship to prefix caching"; the
+    block's identity is its whole token prefix).  Keys are the literal token tuples, not
+    hashes.  A block leaves the map when its refcount reaches zero."""
+
+    def __init__(self, model: BlockModel):
+        self.m = model
+        self.by_prefix: dict[tuple, int] = {}
+        self.prefix_of: dict[int, tuple] = {}
+
+    def new_sequence(self, tokens):
+        B = self.m.B
+        tokens = [int(t) for t in tokens]
+        full = len(tokens) // B
+        hits = []
+        while len(hits) < full:
+            b = self.by_prefix.get(tuple(tokens[:(len(hits) + 1) * B]))
+            if b is None:
+                break
+            hits.append(b)
+        fresh = self.m.allocate(self.m.blocks_needed(len(tokens)) - len(hits))
+        if fresh is None:
+            return None
+        table = self.m.fork(hits) + fresh
+        for j in range(len(hits), full):
+            self.by_prefix[tuple(tokens[:(j + 1) * B])] = table[j]
+            self.prefix_of[table[j]] = tuple(tokens[:(j + 1) * B])
+        return {"table": table, "len": len(tokens)}, len(hits)
+
+    def release(self, seq) -> None:
+        table = list(seq["table"])
+        self.m.release(table)
+        for b in table:
+            if b not in self.m.ref and b in self.prefix_of:
+                del self.by_prefix[self.prefix_of.pop(b)]

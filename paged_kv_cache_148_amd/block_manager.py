@@ -175,3 +175,67 @@ class BlockManager:
             raise AssertionError("free stack holds a block twice")
         if not np.array_equal(free, self._ref == 0):
             raise AssertionError("free stack and zero refcounts disagree")
+
+
+class PrefixCache:
+    """Reuse of full prompt blocks across requests (page "PagedAttention", PidokuInfra topic
+    10, section 5 "The relationship to prefix caching": hash the token ids of each block,
+    keep a hash -> block id map, and point a new sequence's leading blocks that hash to
+    existing blocks at them, raising their refcounts, instead of computing them again).
+
+    Reading: a block's hash covers its own token ids *and* the hash of the block before it,
+    so that "the first N blocks hash to existing blocks" means "the first N * B tokens are
+    those of an earlier prompt" -- K/V of a token depend on every token before it, so a block
+    with the same ids after a different prefix holds different K/V.  Only full prompt blocks
+    are entered; a partly filled last block stays private, so a sequence's own writes never
+    land in a shared block.  Entries leave the map when their block returns to the free
+    stack.
+    """
+
+    def __init__(self, bm: BlockManager):
+        self.bm = bm
+        self._block_of: dict[bytes, int] = {}
+        self._key_of: dict[int, bytes] = {}
+
+    @staticmethod
+    def block_keys(token_ids, block_size: int) -> list:
+        """Chained SHA-256 digests of the full blocks of ``token_ids``."""
+        import hashlib
+        ids = np.asarray(token_ids, dtype=np.int64)
+        keys, prev = [], b""
+        for j in range(len(ids) // block_size):
+            prev = hashlib.sha256(prev + ids[j * block_size:(j + 1) * block_size].tobytes()).digest()
+            keys.append(prev)
+        return keys
+
+    def cached_blocks(self) -> int:
+        return len(self._block_of)
+
+    def new_sequence(self, token_ids):
+        """A sequence for a prompt, reusing its leading cached blocks.
+
+        Returns ``(sequence, hit_blocks)``, or None (changing nothing) if the uncached part
+        cannot be allocated."""
+        bm = self.bm
+        keys = self.block_keys(token_ids, bm.block_size)
+        hits = []
+        for k in keys:
+            b = self._block_of.get(k)
+            if b is None:
+                break
+            hits.append(b)
+        fresh = bm.allocate(bm.blocks_needed(len(token_ids)) - len(hits))
+        if fresh is None:
+            return None
+        table = bm.fork_table(hits) + fresh
+        for j in range(len(hits), len(keys)):   # the new full blocks become reusable
+            self._block_of[keys[j]] = table[j]
+            self._key_of[table[j]] = keys[j]
+        return Sequence(table, len(token_ids)), len(hits)
+
+    def release(self, seq: Sequence) -> None:
+        table = list(seq.table)
+        self.bm.release(seq)
+        for b in table:
+            if self.bm.refcount(b) == 0 and b in self._key_of:
+                del self._block_of[self._key_of.pop(b)]
