@@ -229,3 +229,29 @@ def make_workload(cfg: Config | str, num_seqs: int | None = None, seed: int | No
 
 def numpy_dtype(cfg: Config):
     return np.float32 if cfg.dtype == "f32" else np.uint16
+
+
+# ---------------------------------------------------------------------------
+# request streams for the allocator simulation: Poisson arrivals, log-normal prompt and
+# output lengths (PidokuInfra page, section 10, exercise B)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class RequestStream:
+    arrival: np.ndarray   # int64 step at which each request arrives (non-decreasing)
+    prompt: np.ndarray    # int64 prompt tokens
+    output: np.ndarray    # int64 tokens it will generate (>= 1)
+    max_len: int          # the longest sequence a request may reach (prompt + output <= max_len)
+
+
+def request_stream(seed: int, n: int, rate: float, prompt_median: float, output_median: float,
+                   sigma: float = 1.0, max_len: int = 2048) -> RequestStream:
+    """n requests: exponential gaps of mean 1/rate steps; prompt and output lengths
+    round(median * exp(sigma * z)), z ~ N(0, 1), with 1 <= prompt <= max_len - 1 and
+    1 <= output <= max_len - prompt."""
+    rng = np.random.default_rng(seed)
+    arrival = np.floor(np.cumsum(rng.exponential(1.0 / rate, size=n))).astype(np.int64)
+    prompt = np.clip(np.round(prompt_median * np.exp(sigma * rng.standard_normal(n))), 1, max_len - 1).astype(np.int64)
+    output = np.round(output_median * np.exp(sigma * rng.standard_normal(n))).astype(np.int64)
+    output = np.clip(output, 1, max_len - prompt)
+    return RequestStream(arrival, prompt, output, max_len)
