@@ -71,6 +71,7 @@ struct AttnArgs {
   int S;             // sequences
   unsigned *queue;   // [0]: items taken beyond the grid (zero between calls)
   int persistent;    // 1: persistent workgroups + work queue; 0: one workgroup per possible item
+  float cls_scale;   // length classes of the longest-first schedule: kClasses / (min(P, max_ctx) + 1)
 };
 
 // Work-item order across the chip.  Workgroups go round-robin to the 8 XCDs by their
@@ -281,7 +282,6 @@ struct MfmaSmem {
   alignas(16) float l[2][16][kWaves];
   int bad[2][kWaves];
   u32x4 kst[kWaves][256];   // per-wave staging of one K tile (16 tokens x 16 chunks of 16 B)
-  int red[kWaves * (kClasses + 1)];   // schedule scan
   int nextw[2];             // item indices taken from the queue, two items ahead
 };
 
@@ -301,94 +301,138 @@ struct MItem {
 // partition of each sequence, longest first: the lengths fall into kClasses classes of
 // equal width and a stable counting sort orders the sequences by class.  The longest
 // items start first and the last ones to finish are short, so the workgroups run out of
-// work together.  Every workgroup builds the same order from context_lens.
+// work together.  Every workgroup builds the same order from context_lens (nothing in it
+// depends on timing).
 // LDS (dynamic): pref[S] (inclusive prefix of full-partition items), ctx[S], order[S].
 struct LptSched {
   int total_full;   // items of the full partitions
   int total;        // all items
 };
 
-__device__ __forceinline__ int length_class(int len, int lmax) {
-  return kClasses - 1 - min(kClasses - 1, (int)(((long long)len * kClasses) / ((long long)lmax + 1)));
+// Scratch of the schedule build: sequences go in chunks of 64 (one per lane).
+constexpr int kMaxChunks = kMaxSchedSeqs / 64;
+struct LptSmem {
+  int cnt[kMaxChunks][kClasses];   // class counts per chunk, then their exclusive prefix over chunks
+  int cfull[kMaxChunks];           // full-partition items per chunk, then their exclusive prefix
+  int cstart[kClasses];            // first position of each class in the order
+  int total_full;
+};
+
+// Length class of a last partition: 0 for the longest lengths.  cls_scale = kClasses /
+// (longest possible last partition + 1), so the product stays below kClasses.
+__device__ __forceinline__ int length_class(int len, float cls_scale) {
+  return kClasses - 1 - min(kClasses - 1, (int)((float)len * cls_scale));
 }
 
-__device__ LptSched build_lpt_schedule(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order, int *sm_red) {
+// Full-partition items and length class of sequence i (class kClasses: no sequence).
+__device__ __forceinline__ void classify(const AttnArgs &a, int c, bool valid, int &nfull, int &cls) {
+  const bool ok = c >= 1 && c <= a.max_ctx;
+  const int np = ok ? (c + a.P - 1) / a.P : 1;
+  nfull = valid ? (np - 1) * a.Hkv : 0;
+  cls = valid ? length_class(ok ? c - (np - 1) * a.P : 0, a.cls_scale) : kClasses;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: within each row of 16 lanes by DPP
+// shifts (zeros shifted in), then the row totals carried forward by row broadcasts
+// (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Builds the schedule; ends with a barrier.
+__device__ LptSched build_lpt_schedule(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order, LptSmem &ss) {
   const int S = a.S, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (S + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, S), hi = min(lo + per, S);
-  const int lmax = min(a.P, a.max_ctx);   // the longest possible last partition
-  constexpr int NV = kClasses + 1;        // scanned values: full-partition items, then class counts
-  int v[NV];
+  const int Q = (S + 63) >> 6;
+  constexpr int kPer = kMaxSchedSeqs / kThreads;
+  {
+    int cv[kPer];   // every length in flight at once
 #pragma unroll
-  for (int k = 0; k < NV; ++k) v[k] = 0;
-  for (int i = lo; i < hi; ++i) {
-    const int c = a.ctx[i];
-    sm_ctx[i] = c;
-    const bool ok = c >= 1 && c <= a.max_ctx;
-    const int np = ok ? (c + a.P - 1) / a.P : 1;
-    v[0] += (np - 1) * a.Hkv;
-    sm_pref[i] = v[0];
-    const int cls = length_class(ok ? c - (np - 1) * a.P : 0, lmax);
-#pragma unroll
-    for (int k = 0; k < kClasses; ++k) v[1 + k] += cls == k;
-  }
-  // exclusive prefix of every value over the threads: inclusive scan in the wave, then the
-  // wave totals through LDS
-  int x[NV];
-#pragma unroll
-  for (int k = 0; k < NV; ++k) x[k] = v[k];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int y = __shfl_up(x[k], off);
-      if (lane >= off) x[k] += y;
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + r * kThreads;
+      cv[r] = i < S ? a.ctx[i] : 0;
     }
-  }
-  if (lane == 63) {
 #pragma unroll
-    for (int k = 0; k < NV; ++k) sm_red[wv * NV + k] = x[k];
+    for (int r = 0; r < kPer; ++r) {
+      const int i = tid + r * kThreads;
+      if (i < S) sm_ctx[i] = cv[r];
+    }
   }
   __syncthreads();
-  int base[NV], tot[NV];
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    int before = 0, all = 0;
-    for (int w = 0; w < kWaves; ++w) {
-      const int t = sm_red[w * NV + k];
-      before += w < wv ? t : 0;
-      all += t;
-    }
-    base[k] = before + x[k] - v[k];   // this thread's exclusive prefix
-    tot[k] = all;
-  }
-  // class k's sequences start after all those of the longer classes
-  int cstart = 0;
-#pragma unroll
-  for (int k = 0; k < kClasses; ++k) {
-    base[1 + k] += cstart;
-    cstart += tot[1 + k];
-  }
-  for (int i = lo; i < hi; ++i) {
-    sm_pref[i] += base[0];
-    const int c = sm_ctx[i];
-    const bool ok = c >= 1 && c <= a.max_ctx;
-    const int np = ok ? (c + a.P - 1) / a.P : 1;
-    const int cls = length_class(ok ? c - (np - 1) * a.P : 0, lmax);
-    int pos = 0;
+
+  // per chunk: in-chunk prefix of the full-partition items, and the class counts
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int q = wv; q < Q; q += kWaves) {
+    const int i = 64 * q + lane;
+    const bool valid = i < S;
+    int nfull, cls;
+    classify(a, valid ? sm_ctx[i] : 0, valid, nfull, cls);
+    const int incl = wave_incl_scan(nfull);
+    if (valid) sm_pref[i] = incl;
+    if (lane == 63) ss.cfull[q] = incl;
+    int cnt = 0;
 #pragma unroll
     for (int k = 0; k < kClasses; ++k) {
-      if (cls == k) {
-        pos = base[1 + k];
-        base[1 + k] += 1;
-      }
+      const uint64_t m = __ballot(cls == k);
+      if (lane == k) cnt = __popcll(m);
     }
-    sm_order[pos] = i;
+    if (lane < kClasses) ss.cnt[q][lane] = cnt;
+  }
+  __syncthreads();
+
+  // wave 0: exclusive prefixes over the chunks (lane k: class k; lane kClasses: full
+  // partitions) and the first position of each class
+  if (wv == 0) {
+    int run = 0;
+    if (lane < kClasses) {
+      for (int q = 0; q < Q; ++q) {
+        const int v = ss.cnt[q][lane];
+        ss.cnt[q][lane] = run;
+        run += v;
+      }
+    } else if (lane == kClasses) {
+      for (int q = 0; q < Q; ++q) {
+        const int v = ss.cfull[q];
+        ss.cfull[q] = run;
+        run += v;
+      }
+      ss.total_full = run;
+    }
+    const int tot = lane < kClasses ? run : 0;
+    const int incl = wave_incl_scan(tot);
+    if (lane < kClasses) ss.cstart[lane] = incl - tot;
+  }
+  __syncthreads();
+
+  // per chunk: each sequence's place -- its class's start, the earlier chunks' sequences
+  // of that class, then the earlier lanes' of this chunk (a stable order)
+  for (int q = wv; q < Q; q += kWaves) {
+    const int i = 64 * q + lane;
+    const bool valid = i < S;
+    int nfull, cls;
+    classify(a, valid ? sm_ctx[i] : 0, valid, nfull, cls);
+    uint64_t mine = 0ull;
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) {
+      const uint64_t m = __ballot(cls == k);
+      if (cls == k) mine = m;
+    }
+    if (valid) {
+      sm_pref[i] += ss.cfull[q];
+      sm_order[ss.cstart[cls] + ss.cnt[q][cls] + __popcll(mine & below)] = i;
+    }
   }
   __syncthreads();
   LptSched r;
-  r.total_full = tot[0];
-  r.total = tot[0] + S * a.Hkv;
+  // at most max_parts - 1 full partitions per (sequence, KV head): whatever LDS holds, the
+  // item loop stays bounded
+  r.total_full = min(max(ss.total_full, 0), S * a.Hkv * (a.max_parts - 1));
+  r.total = r.total_full + S * a.Hkv;
   return r;
 }
 
@@ -589,26 +633,27 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
   static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
   constexpr int D = 128;
   __shared__ MfmaSmem sm;
+  __shared__ LptSmem sched_sm;
   extern __shared__ int sm_dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: keeps tile addresses in SGPRs
   const int c16 = lane & 15, grp = lane >> 4;
   int *sm_pref = sm_dyn, *sm_ctx = sm_dyn + a.S, *sm_order = sm_dyn + 2 * a.S;
 
-  // The workgroup's items: it_0 = blockIdx.x, then one index per queue fetch.  The fetch
-  // for it_{k+2} is made while it_k runs, so both the current and the next item are
-  // always known.
+  // The workgroup's items: it_0 = blockIdx.x and it_1 = gridDim.x + blockIdx.x (the longest
+  // items, so a fixed split costs little balance, and the launch makes no queue fetch), then
+  // one index per queue fetch, counted from 2 * gridDim.x.  The fetch for it_{k+2} is made
+  // while it_k runs, so both the current and the next item are always known.
   LptSched sched;
   if (a.persistent) {
-    if (tid == 0) sm.nextw[1] = (int)(gridDim.x + atomicAdd(&a.queue[0], 1u));
-    sched = build_lpt_schedule(a, sm_pref, sm_ctx, sm_order, sm.red);   // ends with a barrier
+    sched = build_lpt_schedule(a, sm_pref, sm_ctx, sm_order, sched_sm);   // ends with a barrier
   } else {
     sched.total_full = 0;
     sched.total = (int)gridDim.x;
   }
   const int total = sched.total;
   int w = (int)blockIdx.x;
-  int wn = a.persistent ? sm.nextw[1] : total;
+  int wn = a.persistent ? (int)(gridDim.x + blockIdx.x) : total;
   if (w < total) {
     MItem cur = item_at<NB>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
     MItem nxt;
@@ -873,7 +918,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
           for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
         }
       }
-      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(gridDim.x + fetched) : total;
+      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(2 * gridDim.x + fetched) : total;
       __syncthreads();
       if (cur.fill == 0)
         mfma_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
@@ -1346,6 +1391,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   a.max_parts = (int)np;
   a.scale_log2 = scale * kLog2e;
   a.S = num_seqs;
+  a.cls_scale = (float)kClasses / (float)((P < max_context_len ? P : max_context_len) + 1);
 
   hipStream_t st = (hipStream_t)stream;
   const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty

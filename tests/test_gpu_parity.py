@@ -550,6 +550,21 @@ def test_work_queue_counters_return_to_zero(name, P):
     H.check_close(first, ref, cfg.dtype, f"queue {name}")
 
 
+@pytest.mark.parametrize("num_seqs", [300, 4096])
+def test_persistent_schedule_many_sequences(num_seqs):
+    # the persistent path's longest-first schedule over many 64-sequence chunks, up to the most
+    # sequences it stages in LDS: every item exactly once, with full and last partitions mixed
+    cfg = workloads.Config("chunks", "bf16", num_seqs, 8, 2, 128, 16, ("uniform", 1, 400), seed=31 + num_seqs)
+    wl = workloads.make_workload(cfg)
+    step = pbatch.step_for(wl)
+    for P in (0, 128):
+        _say("persistent schedule", num_seqs, "P", P)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P)
+        _, _, _, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(H.bits(d["out"]), ref, "bf16", f"chunks S={num_seqs} P={P}")
+
+
 def test_large_batch_uses_fallback_grid():
     # more sequences than the persistent schedule stages in LDS: one workgroup per item
     cfg = workloads.Config("many", "bf16", 4500, 8, 2, 128, 16, ("uniform", 1, 40), seed=77)
