@@ -1202,11 +1202,13 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float *red) 
   return r;
 }
 
+// One workgroup per (head, sequence).  (Four workgroups per head, on slices of the head
+// dimension, were slower: each repeats the scattered (m, l) loads.)
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a) {
   constexpr int CHK = D / 4;            // float4 chunks per row
   constexpr int PL = kThreads / CHK;    // partitions processed side by side
-  extern __shared__ float sm_w[];       // [max_parts] merge weights
+  extern __shared__ float sm_w[];        // [max_parts] merge weights
   __shared__ f32x4 sm_acc[kThreads];
   __shared__ float red[kWaves];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
@@ -1232,7 +1234,7 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
   const int c = tid % CHK, pl = tid / CHK;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4 *po = reinterpret_cast<const f32x4 *>(a.ws_o + base * D) + c;
-#pragma unroll 4
+#pragma unroll 8
   for (int i = pl; i < np; i += PL) acc += sm_w[i] * po[(size_t)i * CHK];
   sm_acc[tid] = acc;
   __syncthreads();
@@ -1242,6 +1244,59 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a)
     const size_t o = ((size_t)s * a.Hq + h) * D + 4 * c;
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_out<T>(a.out, o + e, acc[e] / L);
+  }
+}
+
+// Pass 2 for at most kShortParts partials per head (the partition count is bounded by the
+// host): a workgroup merges kReduceHeads heads of one sequence, a lane per 16-byte chunk of
+// a head's output, with every partial of the lane loaded at once -- three dependent loads
+// (length, (m, l), partials) per workgroup, and a sixteenth of the workgroups of one per
+// (sequence, head).  Same weights and the same ascending partition order as above.
+constexpr int kShortParts = 16;
+constexpr int kReduceHeads = 16;
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_reduce_short_kernel(const AttnArgs a) {
+  constexpr int CH = D / 4;      // 16-byte chunks of fp32 per head: 32 or 16
+  constexpr int HPW = 64 / CH;   // heads a wave merges side by side: 2 or 4
+  const int s = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ctx = a.ctx[s];
+  if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
+  const int np = min((ctx + a.P - 1) / a.P, kShortParts);
+  const int c = lane % CH;
+  const int h_end = min(a.Hq, (int)(blockIdx.x + 1) * kReduceHeads);
+  for (int h = (int)blockIdx.x * kReduceHeads + wv * HPW + lane / CH; h < h_end; h += kWaves * HPW) {
+    const int kvh = h / a.g, j = h % a.g;
+    const float *ml = a.ws_ml + ((size_t)s * a.Hkv + kvh) * a.max_parts * 32 + 2 * j;
+    const f32x4 *po = reinterpret_cast<const f32x4 *>(a.ws_o + ((size_t)s * a.Hq + h) * a.max_parts * D) + c;
+    float m[kShortParts], l[kShortParts];
+    f32x4 o[kShortParts];
+#pragma unroll
+    for (int p = 0; p < kShortParts; ++p) {
+      const bool in = p < np;
+      m[p] = in ? ml[(size_t)p * 32] : kNegInf;
+      l[p] = in ? ml[(size_t)p * 32 + 1] : 0.f;
+      o[p] = in ? po[(size_t)p * CH] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    float M = kNegInf;
+#pragma unroll
+    for (int p = 0; p < kShortParts; ++p) M = fmaxf(M, m[p]);
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < kShortParts; ++p) {
+      const float w = merge_weight(m[p], M);
+      L += w * l[p];
+      acc += w * o[p];
+    }
+    const size_t oi = ((size_t)s * a.Hq + h) * D + 4 * c;
+    if constexpr (sizeof(T) == 4) {
+      *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + oi) = acc / L;
+    } else {
+      u32x2 v;
+      v[0] = pack_bf16x2(acc[0] / L, acc[1] / L);
+      v[1] = pack_bf16x2(acc[2] / L, acc[3] / L);
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + oi) = v;
+    }
   }
 }
 
@@ -1323,9 +1378,16 @@ static int resident_workgroups(Pass1Fn fn, size_t dyn_lds) {
   return (occ > 0 ? occ : 1) * cus;
 }
 
+// Pass 2: the short-count kernel when every head has at most kShortParts partials.
 template <typename T, int D>
-static void launch_reduce(dim3 grid, hipStream_t st, const AttnArgs &a) {
-  hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kThreads), (size_t)a.max_parts * sizeof(float), st, a);
+static void launch_reduce(hipStream_t st, const AttnArgs &a) {
+  if (a.max_parts <= kShortParts) {
+    const dim3 grid((unsigned)((a.Hq + kReduceHeads - 1) / kReduceHeads), (unsigned)a.S);
+    hipLaunchKernelGGL((attn_reduce_short_kernel<T, D>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
+    hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kThreads), (size_t)a.max_parts * sizeof(float), st, a);
+  }
 }
 
 static int64_t parts_for(int64_t max_ctx, int64_t P) { return (max_ctx + P - 1) / P; }
@@ -1431,13 +1493,12 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
     return PKV_ERR_HIP;
   if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   if (np > 1) {
-    const dim3 rgrid((unsigned)num_heads, (unsigned)num_seqs);
     if (bf16) {
-      if (head_dim == 128) launch_reduce<uint16_t, 128>(rgrid, st, a);
-      else launch_reduce<uint16_t, 64>(rgrid, st, a);
+      if (head_dim == 128) launch_reduce<uint16_t, 128>(st, a);
+      else launch_reduce<uint16_t, 64>(st, a);
     } else {
-      if (head_dim == 128) launch_reduce<float, 128>(rgrid, st, a);
-      else launch_reduce<float, 64>(rgrid, st, a);
+      if (head_dim == 128) launch_reduce<float, 128>(st, a);
+      else launch_reduce<float, 64>(st, a);
     }
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
