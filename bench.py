@@ -122,33 +122,47 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     gen_s = time.time() - t_gen
     n_pairs = step.copy_pairs.shape[0]
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    def attend_once():
+        attend(out, q, kc, vc, tables, ctx, step.max_context_len, wl.scale, partition, ws)
 
-    def one_step(i=None):
+    def one_step():
         if n_pairs:
             copy(kc, vc, pairs)
         write(kn, vn, kc, vc, slots)
-        if i is not None:
-            ev[i][0].record()
-        attend(out, q, kc, vc, tables, ctx, step.max_context_len, wl.scale, partition, ws)
-        if i is not None:
-            ev[i][1].record()
+        attend_once()
 
     for _ in range(warmup):
         one_step()
+    # the whole step, `steps` times, by the host clock
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        one_step(i)
+    for _ in range(steps):
+        one_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / steps
+    # The attention call's launch duration: the same call `steps` times back to back between one
+    # pair of events on the launch stream.
+    b2b = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    b2b[0].record()
+    for _ in range(steps):
+        attend_once()
+    b2b[1].record()
+    torch.cuda.synchronize()
+    attn_s = b2b[0].elapsed_time(b2b[1]) / 1e3 / steps
+    # and its spread: events around each launch (they add 3-9 us of their own to each figure)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        attend_once()
+        b.record()
+    torch.cuda.synchronize()
     attn_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    attn_s = float(np.mean(attn_ms)) / 1e3
     nb = algorithmic_bytes(cfg, step)
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
         "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
+        "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3,
         "attention_us_p10": attn_ms[len(attn_ms) // 10] * 1e3, "attention_us_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
         "step_gbs": nb["step"] / step_s / 1e9,
         "kv_gbs_attention": nb["kv"] / attn_s / 1e9,
@@ -325,6 +339,8 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": nb["attention"],
             "launch_us_mean": round(res["attention_us_mean"], 2),
+            "timing": f"HIP events around {args.steps} back-to-back attention launches on the launch stream",
+            "launch_us_events_each": round(res["attention_us_events_mean"], 2),
         },
         "cpu_baseline": cpu,
         "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}

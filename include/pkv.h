@@ -66,7 +66,8 @@ typedef enum { PKV_PATH_NONE = 0, PKV_PATH_VECTOR = 1, PKV_PATH_MFMA = 2 } pkv_p
  * Device values: slots outside [0, num_blocks * block_size) -- including the
  * conventional -1 "no slot" -- are skipped (nothing is written for that token).
  * Slots must be distinct within one call; with duplicates the result is undefined.
- * num_tokens == 0 is a valid no-op.
+ * num_tokens == 0 is a valid no-op.  A row (num_kv_heads * head_dim elements) above
+ * 256 MiB returns PKV_ERR_UNSUPPORTED.
  */
 pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                           const int64_t *slot_mapping, int64_t num_tokens, int32_t num_blocks,

@@ -12,25 +12,44 @@
 
 namespace pkv {
 
-// One workgroup per token (grid-stride beyond the grid).  A slot names one
-// [Hkv, D] row of the pool; consecutive slots are consecutive rows, so the row of
-// slot s = b * B + o starts s * row_vecs 16-byte vectors into the pool.
-__global__ __launch_bounds__(256) void kv_write_kernel(const u32x4 *__restrict__ k_new,
-                                                       const u32x4 *__restrict__ v_new,
-                                                       u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
-                                                       const int64_t *__restrict__ slots, int64_t num_tokens,
-                                                       int row_vecs, int64_t num_slots) {
+// One workgroup per (token, 4 KiB chunk of its row), grid-stride over tokens beyond the
+// grid.  A slot names one [Hkv, D] row of the pool; consecutive slots are consecutive rows,
+// so the row of slot s = b * B + o starts s * row_vecs 16-byte vectors into the pool.  The
+// row loads do not depend on the slot, so they are in flight together with the slot load:
+// one load round trip, then the stores.
+constexpr int kWriteThreads = 128;
+constexpr int kWriteVecs = 2;                               // 16-byte vectors per thread and tensor
+constexpr int kWriteChunk = kWriteThreads * kWriteVecs;     // vectors of a row per workgroup
+__global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(const u32x4 *__restrict__ k_new,
+                                                                 const u32x4 *__restrict__ v_new,
+                                                                 u32x4 *__restrict__ k_cache,
+                                                                 u32x4 *__restrict__ v_cache,
+                                                                 const int64_t *__restrict__ slots,
+                                                                 int64_t num_tokens, int row_vecs, int64_t num_slots) {
+  const int c0 = (int)blockIdx.y * kWriteChunk + (int)threadIdx.x;
   for (int64_t tok = blockIdx.x; tok < num_tokens; tok += gridDim.x) {
     const int64_t slot = slots[tok];
-    if (slot < 0 || slot >= num_slots) continue;  // -1 / out of range: no write
     const u32x4 *ks = k_new + tok * row_vecs;
     const u32x4 *vs = v_new + tok * row_vecs;
+    u32x4 kv[kWriteVecs], vv[kWriteVecs];
+#pragma unroll
+    for (int i = 0; i < kWriteVecs; ++i) {
+      const int c = c0 + i * kWriteThreads;
+      if (c < row_vecs) {
+        kv[i] = ks[c];
+        vv[i] = vs[c];
+      }
+    }
+    if (slot < 0 || slot >= num_slots) continue;  // -1 / out of range: no write
     u32x4 *kd = k_cache + slot * row_vecs;
     u32x4 *vd = v_cache + slot * row_vecs;
-    for (int c = threadIdx.x; c < row_vecs; c += blockDim.x) {
-      const u32x4 kv = ks[c], vv = vs[c];
-      kd[c] = kv;
-      vd[c] = vv;
+#pragma unroll
+    for (int i = 0; i < kWriteVecs; ++i) {
+      const int c = c0 + i * kWriteThreads;
+      if (c < row_vecs) {
+        kd[c] = kv[i];
+        vd[c] = vv[i];
+      }
     }
   }
 }
@@ -121,10 +140,12 @@ extern "C" pkv_status paged_kv_write(const void *k_new, const void *v_new, void 
       !aligned(slot_mapping, 8))
     return PKV_ERR_INVALID_ARG;
   const int64_t elem = dtype == PKV_DTYPE_F32 ? 4 : 2;
-  const int row_vecs = (int)((int64_t)num_kv_heads * head_dim * elem / 16);
-  const int threads = row_vecs >= 256 ? 256 : (row_vecs >= 128 ? 128 : 64);
+  const int64_t row_vecs64 = (int64_t)num_kv_heads * head_dim * elem / 16;
+  const int64_t chunks = (row_vecs64 + kWriteChunk - 1) / kWriteChunk;
+  if (chunks > 65535) return PKV_ERR_UNSUPPORTED;
+  const int row_vecs = (int)row_vecs64;
   const unsigned grid = (unsigned)(num_tokens < (1 << 20) ? num_tokens : (1 << 20));
-  hipLaunchKernelGGL(kv_write_kernel, dim3(grid), dim3(threads), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(kv_write_kernel, dim3(grid, (unsigned)chunks), dim3(kWriteThreads), 0, (hipStream_t)stream,
                      (const u32x4 *)k_new, (const u32x4 *)v_new, (u32x4 *)k_cache, (u32x4 *)v_cache, slot_mapping,
                      num_tokens, row_vecs, (int64_t)num_blocks * block_size);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
