@@ -33,7 +33,7 @@ import workloads  # noqa: E402
 METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak), µs/decode step"
 HBM_PEAK_GBS = 8000.0
 # split-context partition used per workload (0 = one work unit per (sequence, KV head))
-PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": 0}
+PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": 1024}
 MAIN = "mha7b"
 
 

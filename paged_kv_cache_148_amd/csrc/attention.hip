@@ -16,10 +16,10 @@
 // sequences whose context fits one partition are finished in pass 1.
 //
 // Scheduling: the pass-1 kernels are persistent.  As many workgroups as fit on the chip
-// each build, in LDS, the prefix sum of per-sequence item counts from context_lens (so
-// only non-empty items exist).  Workgroup b starts with item b and then takes items in
-// order from a work-queue counter in the workspace until none are left; the last
-// workgroup to finish returns the counters to zero.  A dynamic
+// each build the same item order in LDS from context_lens (so only non-empty items exist):
+// the vector kernel in sequence order, the MFMA kernel longest first.  Workgroups take
+// their first items by index and the rest from a work-queue counter in the workspace until
+// none are left; the last workgroup to finish returns the counters to zero.  A dynamic
 // queue keeps every XCD busy until the end even though the XCDs do not run at identical
 // speeds, and no launch slot is spent on empty partitions.  Batches too large to stage in
 // LDS fall back to one workgroup per possible item.
