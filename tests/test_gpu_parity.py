@@ -464,7 +464,7 @@ def test_split_matches_unsplit_within_tolerance():
 # full-size configurations, in the bench's launch configuration, on sampled outputs
 # ---------------------------------------------------------------------------
 
-BENCH_PARTITION = {"mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": 0}
+from bench import PARTITION as BENCH_PARTITION  # noqa: E402  (the partitions bench.py times)
 
 
 @pytest.mark.parametrize("name", ["mha7b", "gqa70b", "long_splitk", "fork_cow"])
