@@ -330,8 +330,10 @@ def main():
         "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_attention_decode (attn_vec_kernel)" if res["path"] == 1 else
-                      "paged_attention_decode (attn_mfma_kernel)",
+            "kernel": {1: "paged_attention_decode (attn_vec_kernel)",
+                       2: "paged_attention_decode (attn_tile_kernel, MFMA tiles)",
+                       3: "paged_attention_decode (attn_tile_kernel, VALU dots: one query head per KV head)"}.get(
+                           res["path"], "paged_attention_decode"),
             "achieved": round(res["attention_alg_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -53,7 +53,15 @@ typedef enum {
 
 typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
 
-typedef enum { PKV_PATH_NONE = 0, PKV_PATH_VECTOR = 1, PKV_PATH_MFMA = 2 } pkv_path;
+/*
+ * Kernel families of paged_attention_decode:
+ *   PKV_PATH_VECTOR    -- fp32, or head_dim 64: one token row per lane group, q.k by DPP sums;
+ *   PKV_PATH_MFMA      -- bf16, head_dim 128, 2..16 query heads per KV head: 16-token tiles
+ *                         on MFMA, the query-head group as the B operand;
+ *   PKV_PATH_TILE_VALU -- bf16, head_dim 128, one query head per KV head: the same 16-token
+ *                         tile stream with q.k and P.V as fp32 FMAs (q.k summed by DPP).
+ */
+typedef enum { PKV_PATH_NONE = 0, PKV_PATH_VECTOR = 1, PKV_PATH_MFMA = 2, PKV_PATH_TILE_VALU = 3 } pkv_path;
 
 /*
  * paged_kv_write -- write the K/V rows of new tokens into the pool through a slot

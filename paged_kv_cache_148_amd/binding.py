@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libpkv.so")
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, 1, 2, 3
 PKV_DTYPE_F32, PKV_DTYPE_BF16 = 0, 1
-PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA = 0, 1, 2
+PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA, PKV_PATH_TILE_VALU = 0, 1, 2, 3
 
 # every symbol include/pkv.h declares
 EXPORTS = ("paged_kv_write", "paged_attention_decode", "copy_blocks", "pkv_attention_workspace_size",

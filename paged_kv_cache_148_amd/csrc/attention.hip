@@ -25,12 +25,14 @@
 // LDS fall back to one workgroup per possible item.
 //
 // Two pass-1 kernels:
-//   attn_mfma_kernel  (bf16, D = 128, every block size, 1 <= g <= 16): a 16-token tile of
-//     K times the group's Q^T on v_mfma_f32_16x16x32_bf16 gives the score tile; the
-//     probabilities stay in the MFMA result layout and feed v_mfma_f32_16x16x16_bf16
-//     against V^T for P.V.  The head dimension of the P.V product is permuted so that
-//     each lane's V operand is one 16-byte row piece of 4 tokens, regrouped in
-//     registers (no LDS round trip for V).
+//   attn_tile_kernel  (bf16, D = 128, every block size, 1 <= g <= 16): each wave streams
+//     16-token tiles of K and V rows.  With a group of g >= 2 query heads (a real
+//     contraction) a K tile times the group's Q^T on v_mfma_f32_16x16x32_bf16 gives the
+//     score tile; the probabilities stay in the MFMA result layout and feed
+//     v_mfma_f32_16x16x16_bf16 against V^T for P.V, the head dimension permuted so that
+//     each lane's V operand is one 16-byte row piece of 4 tokens regrouped in registers (no
+//     LDS round trip for V).  With one query head per KV head, q.k and P.V are fp32 FMAs on
+//     exactly widened row pieces, q.k summed over a 16-lane row by DPP.
 //   attn_vec_kernel   (everything else: fp32, D = 64): one token
 //     row per D*e/16 lanes, 16-byte loads along head_dim, q.k as fp32 FMAs on exactly
 //     widened elements, row sums by DPP.
@@ -46,7 +48,7 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMfmaDepth = 4;          // MFMA path: tiles per wave in the load ring (NB - 1 ahead)
+constexpr int kTileDepth = 4;          // tile path: tiles per wave in the load ring (NB - 1 ahead)
 constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
 constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
 constexpr int kClasses = 16;            // length classes of the longest-first schedule
@@ -242,9 +244,14 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path: bf16, D = 128, any block size (4 .. 128), a group of 1 to 16 query heads.
+// Tile path: bf16, D = 128, any block size (4 .. 128), a group of 1 to 16 query heads.
 //
-// Lane l of a wave: c16 = l % 16, grp = l / 16.
+// Lane l of a wave: c16 = l % 16, grp = l / 16.  Each tile load gives lane l bytes
+// 16 c16 .. + 15 (head dims 8 c16 .. + 7) of the K and V rows of tile rows 4grp + r.
+// One query head per KV head (VALU): lane l's 8 dims of row 4grp + r times the same 8 dims
+//   of q, summed over the 16 lanes of the row by DPP; P.V adds p(row) times the lane's 8 dims
+//   of the row's V piece, and the lane groups' sums are added at the merge.
+// Groups of 2..16 query heads (MFMA):
 //   QK  (v_mfma_f32_16x16x32_bf16, A = K tile [16 tokens x 32 d], B = Q^T [32 d x 16 heads]):
 //       lane l needs token c16's d-slice 32c + 8grp .. +7 for c = 0..3 and the same
 //       slice of head c16's q row.  K is loaded as whole rows (like V, below) and turned
@@ -278,11 +285,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kBufferConfig);
 }
 
-constexpr int kMfmaOS = 128 + 4;   // padded head stride of the LDS merge buffer
-struct MfmaSmem {
+constexpr int kTileOS = 128 + 4;   // padded head stride of the LDS merge buffer
+struct TileSmem {
   // per-wave states of the item being merged; two sets, alternating between items, so one
   // barrier per item separates the writes of an item from the reads of the one before
-  float o[2][kWaves][16][kMfmaOS];
+  float o[2][kWaves][16][kTileOS];
   alignas(16) float m[2][16][kWaves];   // [head][wave]: one 16-byte read per head
   alignas(16) float l[2][16][kWaves];
   int bad[2][kWaves];
@@ -532,6 +539,16 @@ __device__ __forceinline__ void load_q(const AttnArgs &a, const MItem &it, int c
   for (int c = 0; c < 4; ++c) qd[c] = __builtin_amdgcn_raw_buffer_load_b128(r, (c16 * D + 32 * c + 8 * grp) * 2, 0, 0);
 }
 
+// The q row piece of the VALU path (one query head per KV head): lane (c16, grp) takes head
+// dims 8 c16 .. 8 c16 + 7, the same piece for every grp.
+__device__ __forceinline__ void load_q_row(const AttnArgs &a, const MItem &it, int c16, u32x4 *qd) {
+  constexpr int D = 128;
+  const __amdgpu_buffer_rsrc_t r =
+      buf_rsrc(reinterpret_cast<const uint16_t *>(a.q) + ((size_t)it.s * a.Hq + it.kvh) * D,
+               it.fill == 0 ? (uint32_t)(D * 2) : 0u);
+  qd[0] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * c16, 0, 0);
+}
+
 // Item index -> item.  Persistent launch: from the LDS schedule; otherwise one item per
 // workgroup in the fixed grid order, with the length read from memory.
 // Item fields come from LDS and memory (vector registers); they are the same in every lane.
@@ -565,8 +582,8 @@ __device__ __forceinline__ MItem item_at(const AttnArgs &a, int w, const LptSche
 // Merge of the four waves' states of an item, then its output (normalised, or a partial
 // state for the second pass).  Thread t covers head t / 16 of the group and head dims
 // 8 (t % 16) .. +7: ten independent LDS reads and one wait, then 16-byte stores.
-__device__ __forceinline__ void mfma_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
-                                            const float (*sm_l)[kWaves], const float (*sm_o)[16][kMfmaOS],
+__device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
+                                            const float (*sm_l)[kWaves], const float (*sm_o)[16][kTileOS],
                                             const int *sm_bad) {
   constexpr int D = 128;
   const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 8;
@@ -641,11 +658,15 @@ __device__ __forceinline__ void mfma_finish(const AttnArgs &a, const MItem &it, 
 // 16i + c16 (8 bytes; instruction i: 16 dims x 16 tokens, 512 B contiguous at B = 16) straight
 // into its A operand: no LDS staging and no byte permutes.  The accumulator of MFMA i then
 // holds dims 16i + 4grp + r.  Blocks of 16 slots or more.
-template <int B, int NB, bool HM>
-__global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
+// MF: q.K and P.V as MFMA tiles with the query-head group as the B operand (groups of 2 to 16
+// heads, a real contraction).  !MF: one query head per KV head -- the tiles' K and V row pieces
+// meet q and P in fp32 FMAs on exactly widened elements, and q.k is summed over a 16-lane row
+// by DPP (an MFMA would leave 15 of its 16 columns empty).
+template <int B, int NB, bool HM, bool MF>
+__global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
   constexpr int D = 128;
-  __shared__ MfmaSmem sm;
+  __shared__ TileSmem sm;
   __shared__ LptSmem sched_sm;
   extern __shared__ int sm_dyn[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -692,8 +713,16 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
     int tb_cur[BPT], tb_ahead[BPT], tb_next[BPT], tb_next_ahead[BPT];
     table_chunks<B>(a, cur, 0, wave, lane, tb_cur);
     table_chunks<B>(a, cur, 1, wave, lane, tb_ahead);
+    // q operands: MF, head c16 of the group in the B layout; !MF on the head-major layout, the
+    // item's head at the K chunks lane group grp holds (dims 32c + 8grp); !MF on the row
+    // layout, dims 8 c16 .. + 7
+    auto load_item_q = [&](const MItem &it, u32x4 *qd) {
+      if constexpr (MF) load_q(a, it, c16, grp, qd);
+      else if constexpr (HM) load_q(a, it, 0, grp, qd);
+      else load_q_row(a, it, c16, qd);
+    };
     u32x4 qop[4], qnext[4];
-    load_q(a, cur, c16, grp, qop);
+    load_item_q(cur, qop);
     int bad_cur = 0, bad_next = 0;
 
     // Loads of tile i of an item (zero-range descriptors past its live tiles).
@@ -770,13 +799,86 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       load_tile(nxt, i, phys, kd, vd, vd2);
     };
 
+    // accumulators: MF, MFMA i's 16x16 tile; !MF, head dims 8 c16 + 4i + e of this lane group's
+    // tokens (e = 0..3), summed over the lane groups at the merge
+    constexpr int NACC = MF ? 8 : 2;
     float m = kNegInf, lsum = 0.f;
-    f32x4 acc[8];
+    f32x4 acc[NACC];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
       const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      if constexpr (!MF && HM) {
+        // head-major, one query head: lane (c16, grp) holds K chunks 4c + grp of tile row c16
+        // and the V pieces of rows 4grp .. 4grp + 3 at dims 16j + c16
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            d = __builtin_fmaf(bf16_lo(qop[c][w2]), bf16_lo(kr[c][w2]), d);
+            d = __builtin_fmaf(bf16_hi(qop[c][w2]), bf16_hi(kr[c][w2]), d);
+          }
+        }
+        d += __shfl_xor(d, 16);   // the four lane groups' 32 dims each
+        d += __shfl_xor(d, 32);
+        const int tk = tok0 + c16;
+        const float sv = tk >= cur.t0 && tk < cur.t1 ? d * a.scale_log2 : kNegInf;
+        const float mnew = fmaxf(m, group_max16(sv));
+        const float alpha = merge_weight(m, mnew);
+        const float pt = sv == kNegInf ? 0.f : fast_exp2(sv - mnew);
+        lsum = lsum * alpha + group_sum<16>(pt);   // the same in every lane
+        if (alpha != 1.f) {
+#pragma unroll
+          for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
+        }
+        m = mnew;
+        if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
+          uint32_t keep01 = 0u, keep23 = 0u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tr = tok0 + 4 * grp + r;
+            const uint32_t half = tr >= cur.t0 && tr < cur.t1 ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
+            if (r < 2) keep01 |= half; else keep23 |= half;
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
+        }
+        float pr[4];   // p of rows 4grp + r, held by lane 4grp + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = __shfl(pt, 4 * grp + r);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t w = vr2[j][r >> 1];
+            acc[j >> 2][j & 3] = __builtin_fmaf(pr[r], (r & 1) ? bf16_hi(w) : bf16_lo(w), acc[j >> 2][j & 3]);
+          }
+        }
+        return;
+      }
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!MF) {
+        // lane (c16, grp) holds dims 8 c16 .. + 7 of tile row 4 grp + r in kr[r]: a dot product
+        // over its 8 dims, then the sum over the 16 lanes of the row
+        float qf[8];
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          qf[2 * w2] = bf16_lo(qop[0][w2]);
+          qf[2 * w2 + 1] = bf16_hi(qop[0][w2]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float d = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            d = __builtin_fmaf(qf[2 * w2], bf16_lo(kr[r][w2]), d);
+            d = __builtin_fmaf(qf[2 * w2 + 1], bf16_hi(kr[r][w2]), d);
+          }
+          sc[r] = group_sum<16>(d);
+        }
+      } else {
       u32x4 kop[4];
       if constexpr (HM) {
 #pragma unroll
@@ -794,13 +896,14 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
       }
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
                                                      __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
+      }
 
-      // scores of tile rows 4grp + r for head c16; positions outside [t0, t1) are masked
+      // scores of tile rows 4grp + r (for head c16 on the MFMA path); positions outside
+      // [t0, t1) are masked
       float sv[4], mx = kNegInf;
       uint32_t keep01 = 0u, keep23 = 0u;   // head-major V: halves of the tokens in range
 #pragma unroll
@@ -835,9 +938,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       lsum = lsum * alpha + ps;
       if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+        for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
       }
       m = mnew;
+
+      if constexpr (!MF) {
+        // P.V: each lane adds p(row) times its 8 dims of the row's V piece
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) {
+            acc[w2 >> 1][2 * (w2 & 1)] = __builtin_fmaf(pr[r], bf16_lo(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1)]);
+            acc[w2 >> 1][2 * (w2 & 1) + 1] =
+                __builtin_fmaf(pr[r], bf16_hi(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1) + 1]);
+          }
+        }
+        return;
+      }
 
       const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
       const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
@@ -874,7 +991,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       nxt = item_at<NB>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
       table_chunks<B>(a, nxt, 0, wave, lane, tb_next);
       table_chunks<B>(a, nxt, 1, wave, lane, tb_next_ahead);
-      load_q(a, nxt, c16, grp, qnext);
+      load_item_q(nxt, qnext);
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
       // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
       // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
@@ -911,16 +1028,45 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
         if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
       }
 
-      // merge the waves' states of it_k (the next item's first loads are in flight)
-      float lh = lsum + __shfl_xor(lsum, 16);
-      lh += __shfl_xor(lh, 32);
+      // merge the waves' states of it_k (the next item's first loads are in flight); the item's
+      // sum is spread over the lane groups except on the head-major VALU path
+      float lh = lsum;
+      if constexpr (MF || !HM) {
+        lh += __shfl_xor(lh, 16);
+        lh += __shfl_xor(lh, 32);
+      }
       const int mb = k & 1;
-      if (grp == 0) {
-        sm.m[mb][c16][wave] = m;
-        sm.l[mb][c16][wave] = lh;
+      if constexpr (MF) {
+        if (grp == 0) {
+          sm.m[mb][c16][wave] = m;
+          sm.l[mb][c16][wave] = lh;
+        }
+      } else if (lane == 0) {   // one head: m is the same in every lane
+        sm.m[mb][0][wave] = m;
+        sm.l[mb][0][wave] = lh;
       }
       if (lane == 0) sm.bad[mb][wave] = bad_cur;
-      if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
+      if constexpr (!MF) {   // the lane groups' sums, then dims 8 c16 .. + 7 from lane group 0
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc[i][e];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[i][e] = x;
+          }
+        }
+        if (grp == 0) {
+          if constexpr (HM) {   // dims 16j + c16
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sm.o[mb][wave][0][16 * j + c16] = acc[j >> 2][j & 3];
+          } else {              // dims 8 c16 .. + 7
+            *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][0][8 * c16]) = acc[0];
+            *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][0][8 * c16 + 4]) = acc[1];
+          }
+        }
+      } else if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][c16][16 * i + 4 * grp]) = acc[i];
       } else {              // MFMA i holds dims 32grp + 8r + i
@@ -934,7 +1080,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(2 * gridDim.x + fetched) : total;
       __syncthreads();
       if (cur.fill == 0)
-        mfma_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
+        tile_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
       else if (cur.fill != 3)
         fill_group<uint16_t, D>(a, cur.s, cur.kvh * a.g, a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
       if (wn >= total) break;
@@ -955,7 +1101,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_kernel(const AttnArgs a) {
       m = kNegInf;
       lsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
   }
   if (a.persistent) queue_done(a.queue);
@@ -1311,7 +1457,7 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   if (D != 64 && D != 128) return PKV_PATH_NONE;
   if (B != 4 && B != 8 && B != 16 && B != 32 && B != 64 && B != 128) return PKV_PATH_NONE;
   const int g = Hq / Hkv;
-  if (dt == PKV_DTYPE_BF16 && D == 128 && g <= 16) return PKV_PATH_MFMA;
+  if (dt == PKV_DTYPE_BF16 && D == 128 && g <= 16) return g == 1 ? PKV_PATH_TILE_VALU : PKV_PATH_MFMA;
   return B <= 32 && vec_group(g) ? PKV_PATH_VECTOR : PKV_PATH_NONE;
 }
 
@@ -1319,7 +1465,8 @@ static pkv_path select_path(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
 static pkv_path select_path_head_major(int Hq, int Hkv, int D, int B, pkv_dtype dt) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return PKV_PATH_NONE;
   if (dt != PKV_DTYPE_BF16 || D != 128 || Hq / Hkv > 16) return PKV_PATH_NONE;
-  return B == 16 || B == 32 || B == 64 || B == 128 ? PKV_PATH_MFMA : PKV_PATH_NONE;
+  if (B != 16 && B != 32 && B != 64 && B != 128) return PKV_PATH_NONE;
+  return Hq == Hkv ? PKV_PATH_TILE_VALU : PKV_PATH_MFMA;
 }
 
 typedef void (*Pass1Fn)(AttnArgs);
@@ -1344,25 +1491,32 @@ static Pass1Fn vec_fn(int g, int B) {
   }
 }
 
+template <bool MF>
+static Pass1Fn tile_fn(int B) {
+  switch (B) {
+    case 4: return attn_tile_kernel<4, kTileDepth, false, MF>;
+    case 8: return attn_tile_kernel<8, kTileDepth, false, MF>;
+    case 16: return attn_tile_kernel<16, kTileDepth, false, MF>;
+    case 32: return attn_tile_kernel<32, kTileDepth, false, MF>;
+    case 64: return attn_tile_kernel<64, kTileDepth, false, MF>;
+    default: return attn_tile_kernel<128, kTileDepth, false, MF>;
+  }
+}
+
+template <bool MF>
+static Pass1Fn tile_hm_fn(int B) {
+  switch (B) {
+    case 16: return attn_tile_kernel<16, kTileDepth, true, MF>;
+    case 32: return attn_tile_kernel<32, kTileDepth, true, MF>;
+    case 64: return attn_tile_kernel<64, kTileDepth, true, MF>;
+    default: return attn_tile_kernel<128, kTileDepth, true, MF>;
+  }
+}
+
 static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major) {
-  if (head_major) {
-    switch (B) {
-      case 16: return attn_mfma_kernel<16, kMfmaDepth, true>;
-      case 32: return attn_mfma_kernel<32, kMfmaDepth, true>;
-      case 64: return attn_mfma_kernel<64, kMfmaDepth, true>;
-      default: return attn_mfma_kernel<128, kMfmaDepth, true>;
-    }
-  }
-  if (path == PKV_PATH_MFMA) {
-    switch (B) {
-      case 4: return attn_mfma_kernel<4, kMfmaDepth, false>;
-      case 8: return attn_mfma_kernel<8, kMfmaDepth, false>;
-      case 16: return attn_mfma_kernel<16, kMfmaDepth, false>;
-      case 32: return attn_mfma_kernel<32, kMfmaDepth, false>;
-      case 64: return attn_mfma_kernel<64, kMfmaDepth, false>;
-      default: return attn_mfma_kernel<128, kMfmaDepth, false>;
-    }
-  }
+  if (head_major) return path == PKV_PATH_TILE_VALU ? tile_hm_fn<false>(B) : tile_hm_fn<true>(B);
+  if (path == PKV_PATH_MFMA) return tile_fn<true>(B);
+  if (path == PKV_PATH_TILE_VALU) return tile_fn<false>(B);
   if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
   return D == 128 ? vec_fn<float, 128>(g, B) : vec_fn<float, 64>(g, B);
 }
@@ -1478,7 +1632,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   int64_t grid = items;
   a.persistent = 0;
   if (num_seqs <= kMaxSchedSeqs) {
-    dyn_lds = (path == PKV_PATH_MFMA ? 3 : 2) * (size_t)num_seqs * sizeof(int);
+    dyn_lds = (path == PKV_PATH_VECTOR ? 2 : 3) * (size_t)num_seqs * sizeof(int);
     const int resident = resident_workgroups(fn, dyn_lds);
     if (resident > 0) {
       a.persistent = 1;

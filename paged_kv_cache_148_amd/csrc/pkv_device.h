@@ -74,4 +74,13 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over aligned groups of 16 lanes; every lane of a group gets it.
+__device__ __forceinline__ float group_max16(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppRor4>(x));
+  x = fmaxf(x, dpp<kDppRor8>(x));
+  return x;
+}
+
 }  // namespace pkv

@@ -9,7 +9,8 @@ import pytest
 
 from paged_kv_cache_148_amd import binding
 from paged_kv_cache_148_amd.binding import (PKV_DTYPE_BF16, PKV_DTYPE_F32, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
-                                            PKV_OK, PKV_PATH_MFMA, PKV_PATH_NONE, PKV_PATH_VECTOR)
+                                            PKV_OK, PKV_PATH_MFMA, PKV_PATH_NONE, PKV_PATH_TILE_VALU,
+                                            PKV_PATH_VECTOR)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -53,7 +54,7 @@ def test_workspace_size(L):
 
 def test_path_selection_head_major(L):
     assert binding.attention_path_head_major(64, 8, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA
-    assert binding.attention_path_head_major(32, 32, 128, 128, PKV_DTYPE_BF16) == PKV_PATH_MFMA
+    assert binding.attention_path_head_major(32, 32, 128, 128, PKV_DTYPE_BF16) == PKV_PATH_TILE_VALU   # g = 1
     assert binding.attention_path_head_major(32, 8, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE    # below a tile
     assert binding.attention_path_head_major(8, 8, 128, 16, PKV_DTYPE_F32) == PKV_PATH_NONE     # bf16 only
     assert binding.attention_path_head_major(8, 8, 64, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE
@@ -63,7 +64,7 @@ def test_path_selection_head_major(L):
 def test_path_selection(L):
     assert binding.attention_path(64, 8, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA
     assert binding.attention_path(32, 8, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA
-    assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_MFMA     # g = 1 too
+    assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_TILE_VALU   # g = 1: no MFMA
     assert binding.attention_path(16, 1, 128, 32, PKV_DTYPE_BF16) == PKV_PATH_MFMA      # g = 16
     assert binding.attention_path(32, 32, 128, 16, PKV_DTYPE_F32) == PKV_PATH_VECTOR
     assert binding.attention_path(4, 4, 64, 4, PKV_DTYPE_F32) == PKV_PATH_VECTOR
@@ -74,7 +75,8 @@ def test_path_selection(L):
     assert binding.attention_path(64, 2, 128, 8, PKV_DTYPE_BF16) == PKV_PATH_NONE   # g = 32
     assert binding.attention_path(6, 4, 128, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE   # 6 % 4 != 0
     assert binding.attention_path(8, 8, 96, 16, PKV_DTYPE_BF16) == PKV_PATH_NONE    # head_dim
-    assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_BF16) == PKV_PATH_MFMA   # large blocks: MFMA only
+    assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_BF16) == PKV_PATH_TILE_VALU   # large blocks: tile kernel
+    assert binding.attention_path(16, 8, 128, 64, PKV_DTYPE_BF16) == PKV_PATH_MFMA
     assert binding.attention_path(64, 8, 128, 128, PKV_DTYPE_BF16) == PKV_PATH_MFMA
     assert binding.attention_path(8, 8, 128, 64, PKV_DTYPE_F32) == PKV_PATH_NONE    # no vector path past 32
     assert binding.attention_path(8, 8, 64, 128, PKV_DTYPE_BF16) == PKV_PATH_NONE

@@ -197,9 +197,10 @@ SHAPES = [
     ("bf16", 4, 16, 2, 64, 8, (1, 200)),      # vector, g = 8
     ("bf16", 4, 6, 2, 128, 8, (1, 200)),      # MFMA, g = 3, B = 8: two blocks per tile
     ("bf16", 4, 8, 2, 128, 4, (1, 200)),      # MFMA, g = 4, B = 4: four blocks per tile
-    ("bf16", 4, 8, 8, 128, 32, (1, 300)),     # MHA (g = 1) on the MFMA path, B = 32
-    ("bf16", 4, 8, 8, 128, 8, (1, 300)),      # MHA on the MFMA path, B = 8
-    ("bf16", 3, 4, 4, 128, 16, (4200, 9000)), # g = 1, MFMA, more than 64 tiles per wave
+    ("bf16", 4, 8, 8, 128, 32, (1, 300)),     # MHA (g = 1) on the VALU tile path, B = 32
+    ("bf16", 4, 8, 8, 128, 8, (1, 300)),      # MHA on the VALU tile path, B = 8
+    ("bf16", 3, 4, 4, 128, 16, (4200, 9000)), # g = 1, VALU tiles, more than 64 tiles per wave
+    ("bf16", 4, 8, 8, 128, 4, (1, 300)),      # g = 1, B = 4: four blocks per tile
     ("bf16", 5, 32, 4, 128, 64, (1, 700)),    # B = 64, g = 8
     ("bf16", 4, 8, 8, 128, 128, (1, 900)),    # B = 128, g = 1
     ("bf16", 3, 16, 2, 128, 128, (1, 2600)),  # B = 128, g = 8, more than 64 tiles per wave
@@ -372,6 +373,7 @@ HM_SHAPES = [
     (4, 24, 8, 32, (1, 500), (0, 96)),      # g = 3, B = 32
     (3, 16, 4, 128, (1, 1500), (0, 256)),   # g = 4, B = 128
     (3, 8, 2, 64, (4200, 9000), (0, 512)),  # more than 64 tiles per wave
+    (3, 4, 4, 128, (4200, 9000), (0, 512)), # g = 1 (VALU tiles), more than 64 tiles per wave
 ]
 
 
@@ -394,8 +396,9 @@ def test_head_major_attention_parity(shape):
         H.check_close(H.bits(d["out"]), ref, "bf16", f"head-major {shape} P={P}")
 
 
-def test_head_major_unread_slots_and_padding_never_read():
-    cfg = workloads.Config("hm", "bf16", 6, 32, 4, 128, 16, ("uniform", 1, 200), seed=611)
+@pytest.mark.parametrize("heads", [(32, 4), (8, 8)], ids=["g8", "g1"])
+def test_head_major_unread_slots_and_padding_never_read(heads):
+    cfg = workloads.Config("hm", "bf16", 6, heads[0], heads[1], 128, 16, ("uniform", 1, 200), seed=611)
     wl = workloads.make_workload(cfg)
     step = pbatch.step_for(wl)
     import torch
@@ -428,14 +431,15 @@ def test_head_major_unread_slots_and_padding_never_read():
         assert H.bits(d["out"]).tobytes() == clean.tobytes()
 
 
-def test_head_major_full_size_sampled_parity():
-    wl = _wl("gqa70b")
+@pytest.mark.parametrize("name", ["gqa70b", "mha7b"])
+def test_head_major_full_size_sampled_parity(name):
+    wl = _wl(name)
     step = pbatch.step_for(wl)
     cfg = wl.cfg
     rng = np.random.default_rng(13)
     items = np.unique(rng.integers(0, cfg.num_seqs * cfg.num_heads, size=96))
-    for P in (0, 2048):
-        _say("head-major gqa70b sampled", "P", P)
+    for P in ((0, 2048) if name == "gqa70b" else (0,)):
+        _say("head-major sampled", name, "P", P)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P, do_attn=False)
         khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])
@@ -444,7 +448,7 @@ def test_head_major_full_size_sampled_parity():
         o, kc, vc, _ = H.oracle_step(wl, "steady", P, attend=False)
         ref = oracle.attention(wl.q, kc, vc, o["block_tables"], o["context_lens"], wl.scale, P, items)
         got = H.bits(d["out"]).reshape(cfg.num_seqs * cfg.num_heads, -1)[items]
-        H.check_close(got, ref, "bf16", f"head-major gqa70b P={P}")
+        H.check_close(got, ref, "bf16", f"head-major {name} P={P}")
         del khm, vhm
 
 
