@@ -20,6 +20,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -50,12 +51,22 @@ def algorithmic_bytes(cfg, step) -> dict:
     return {"kv": kv, "attention": attn, "write": write, "copy": copy, "step": attn + write + copy}
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and whitespace (the sources hold no string literal with //
+    or /*): a change of comments or layout leaves the hash alone, a change of code does not."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_source_hash() -> str:
+    """sha256 over the code of paged_kv_cache_148_amd/csrc/* (comments and whitespace removed),
+    first 16 hex digits: the key of the committed counter records."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_148_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

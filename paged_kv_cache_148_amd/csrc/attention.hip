@@ -879,27 +879,27 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
           sc[r] = group_sum<16>(d);
         }
       } else {
-      u32x4 kop[4];
-      if constexpr (HM) {
+        u32x4 kop[4];
+        if constexpr (HM) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kop[c] = kr[c];   // loaded in the A layout
-      } else {
-        // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t
-        // sits at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token,
-        // 16 chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of
-        // 64 banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
+          for (int c = 0; c < 4; ++c) kop[c] = kr[c];   // loaded in the A layout
+        } else {
+          // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t
+          // sits at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token,
+          // 16 chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of
+          // 64 banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * grp + r;
-          kst[t * 16 + (c16 ^ t)] = kr[r];
+          for (int r = 0; r < 4; ++r) {
+            const int t = 4 * grp + r;
+            kst[t * 16 + (c16 ^ t)] = kr[r];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
-                                                     __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
+        for (int c = 0; c < 4; ++c)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
+                                                       __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
       }
 
       // scores of tile rows 4grp + r (for head c16 on the MFMA path); positions outside
