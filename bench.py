@@ -174,7 +174,8 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
         "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
         "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3,
-        "attention_us_p10": attn_ms[len(attn_ms) // 10] * 1e3, "attention_us_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
+        "attention_us_events_p10": attn_ms[len(attn_ms) // 10] * 1e3,
+        "attention_us_events_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
         "step_gbs": nb["step"] / step_s / 1e9,
         "kv_gbs_attention": nb["kv"] / attn_s / 1e9,
         "attention_alg_gbs": nb["attention"] / attn_s / 1e9,
@@ -290,7 +291,8 @@ def main():
         for B in (8, 16, 32, 64, 128):
             r, _, _ = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, B)
             keep = ("block_size", "internal_frag", "table_entries_mean", "table_entries_max", "path", "pool_blocks",
-                    "attention_us_mean", "attention_us_p10", "attention_us_p90", "us_per_step", "kv_gbs_attention",
+                    "attention_us_mean", "attention_us_events_p10", "attention_us_events_p90", "us_per_step",
+                    "kv_gbs_attention",
                     "attention_alg_gbs", "attention_hbm_frac")
             sweep.append({k: (round(r[k], 4) if isinstance(r[k], float) else r[k]) for k in keep})
             print(f"[bench] {args.workload} B={B}: attention {r['attention_us_mean']:.1f} us, "
