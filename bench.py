@@ -94,7 +94,7 @@ def block_stats(cfg, step) -> dict:
 
 
 def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered",
-            block_size: int | None = None):
+            block_size: int | None = None, flush_mall: str | None = None):
     import torch
     from paged_kv_cache_148_amd import batch, binding
 
@@ -161,19 +161,28 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     b2b[1].record()
     torch.cuda.synchronize()
     attn_s = b2b[0].elapsed_time(b2b[1]) / 1e3 / steps
-    # and its spread: events around each launch (they add 3-9 us of their own to each figure)
+    # and its spread: events around each launch (they add 3-9 us of their own to each figure).
+    # flush_mall: 512 MB are read ("read") or written ("write") before each launch, outside its
+    # events, so that no K/V byte can come from the 256 MB Infinity Cache; a written flush also
+    # leaves the cache full of dirty lines that the launch's own stores then have to evict
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev) if flush_mall else None
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for a, b in ev:
+        if flush_mall == "write":
+            flush.fill_(1)
+        elif flush_mall == "read":
+            flush.amax()
         a.record()
         attend_once()
         b.record()
     torch.cuda.synchronize()
     attn_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    del flush
     nb = algorithmic_bytes(cfg, step)
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
         "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
-        "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3,
+        "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3, "mall_flushed_per_launch": flush_mall,
         "attention_us_events_p10": attn_ms[len(attn_ms) // 10] * 1e3,
         "attention_us_events_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
         "step_gbs": nb["step"] / step_s / 1e9,
@@ -269,6 +278,8 @@ def main():
                          "head_major: the shuffled pool in the head-major cache layout")
     ap.add_argument("--block-size", type=int, default=None,
                     help="run the workload with this block size instead of its configured one")
+    ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
+                    help="read or write 512 MB before each per-launch-timed attention call (outside its events)")
     ap.add_argument("--sweep-block-size", action="store_true",
                     help="time the workload at block sizes 8..128 and print one JSON line of the sweep")
     args = ap.parse_args()
@@ -302,7 +313,8 @@ def main():
                           "steps": args.steps, "warmup": args.warmup, "results": sweep,
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
-    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size)
+    res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
+                            args.flush_mall)
     print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step, attention {res['attention_us_mean']:.1f} us, "
           f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
@@ -313,7 +325,7 @@ def main():
             if name == args.workload:
                 continue
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
-                r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name])
+                r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
                 others[f"{name}/{w}" if name == "fork_cow" else name] = r
                 print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step, attention {r['attention_us_mean']:.1f} us,"
                       f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
