@@ -1,0 +1,44 @@
+"""CPU checks of bench.py's accounting: the algorithmic byte counts behind `value` and the
+roofline, and the key that ties the committed counter records to the kernel code."""
+import types
+
+import numpy as np
+
+import bench
+
+
+def _cfg(**kw):
+    base = dict(elem_bytes=2, num_seqs=2, num_heads=8, num_kv_heads=2, head_dim=128, block_size=16)
+    base.update(kw)
+    return types.SimpleNamespace(**base)
+
+
+def test_algorithmic_bytes_by_hand():
+    # two sequences of 17 and 32 tokens (2 + 2 blocks of 16), one new token each, one copy pair
+    step = types.SimpleNamespace(context_lens=np.array([17, 32]), slot_mapping=np.array([5, 40]),
+                                 copy_pairs=np.array([[3, 7]]))
+    nb = bench.algorithmic_bytes(_cfg(), step)
+    kv = (17 + 32) * 2 * 2 * 128 * 2            # K and V rows of every attended position, per KV head
+    q_out = 2 * 2 * 8 * 128 * 2                 # q read and out written, every query head
+    tables = 4 * (2 + 2)                        # one int32 entry per attended block
+    lengths = 4 * 2
+    assert nb["kv"] == kv
+    assert nb["attention"] == kv + q_out + tables + lengths
+    assert nb["write"] == 2 * (2 * 2 * 128 * 2) * 2 + 8 * 2   # rows read and written, K and V, + slots
+    assert nb["copy"] == 2 * 2 * 1 * 16 * 2 * 128 * 2 + 16   # a block read and written, K and V, + pair
+    assert nb["step"] == nb["attention"] + nb["write"] + nb["copy"]
+
+
+def test_gqa_reads_kv_once_per_kv_head():
+    step = types.SimpleNamespace(context_lens=np.array([100]), slot_mapping=np.array([0]),
+                                 copy_pairs=np.zeros((0, 2), np.int64))
+    g8 = bench.algorithmic_bytes(_cfg(num_seqs=1, num_heads=64, num_kv_heads=8), step)
+    g1 = bench.algorithmic_bytes(_cfg(num_seqs=1, num_heads=8, num_kv_heads=8), step)
+    assert g8["kv"] == g1["kv"]                 # 64 query heads over 8 KV heads move no more K/V
+
+
+def test_source_key_ignores_comments_and_layout():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    assert bench._code_only(code) == bench._code_only("/* a note */ int  f(int x)\n{ return x + 1; }")
+    assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
+    assert len(bench.kernel_source_hash()) == 16
