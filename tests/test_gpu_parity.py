@@ -244,6 +244,30 @@ def test_single_token_returns_v_exactly(name):
         assert out[s].tobytes() == np.repeat(wl.v_new[s], g, axis=0).tobytes()
 
 
+@pytest.mark.parametrize("name,P", [("mha7b", 0), ("mha7b", 128), ("gqa70b", 0), ("gqa70b", 256),
+                                    ("tiny_fp32", 8)])
+def test_peaked_and_uniform_softmax(name, P):
+    # scores 32 times their usual spread (near one-hot weights: the running-max rescaling does the
+    # work), then q = 0 (every weight equal: the output is the mean of the attended V rows); the
+    # VALU, MFMA and vector paths, unsplit and split
+    for case in ("peaked", "uniform"):
+        wl = _wl(name, num_seqs=6)
+        if case == "peaked":   # q times 32: a power of two, so the scaled q is exact in bf16 too
+            if wl.q.dtype == np.uint16:
+                f = (wl.q.astype(np.uint32) << 16).view(np.float32) * np.float32(32.0)
+                wl.q[...] = (f.view(np.uint32) >> 16).astype(np.uint16)
+            else:
+                wl.q *= np.float32(32.0)
+        else:
+            wl.q[...] = 0
+        step = pbatch.step_for(wl)
+        _say("softmax", case, name, "P", P)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P)
+        _, _, _, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(H.bits(d["out"]), ref, wl.cfg.dtype, f"{case} {name} P={P}")
+
+
 @pytest.mark.parametrize("name,P", [("mha7b", 0), ("gqa70b", 256), ("tiny_fp32", 8)])
 def test_block_permutation_invariance_bitwise(name, P):
     wl = _wl(name, num_seqs=6)
