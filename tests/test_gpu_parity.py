@@ -476,6 +476,22 @@ def test_head_major_full_size_sampled_parity(name):
         del khm, vhm
 
 
+@pytest.mark.parametrize("heads", [(4, 4), (8, 2)], ids=["g1", "g4"])
+def test_most_partitions_per_head(heads):
+    # 131072 tokens in 16-token partitions: 8192 partials per head, the most the merge stages in
+    # LDS, plus a short sequence that finishes in pass 1
+    Hq, Hkv = heads
+    ctx = np.array([131072, 9], np.int64)
+    cfg = workloads.Config("maxparts", "bf16", 2, Hq, Hkv, 128, 16, ("uniform", 1, 2), seed=71 + Hq)
+    wl = workloads.make_workload(cfg, ctx_override=ctx)
+    step = pbatch.step_for(wl)
+    _say("most partitions", heads, ctx.tolist())
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, 16)
+    _, _, _, ref = H.oracle_step(wl, "steady", 16)
+    H.check_close(H.bits(d["out"]), ref, "bf16", f"8192 partitions {heads}")
+
+
 def test_split_matches_unsplit_within_tolerance():
     wl = _wl("gqa70b", num_seqs=10)
     step = pbatch.step_for(wl)
