@@ -321,7 +321,7 @@ def main():
     del wl
     others = {}
     if not args.only_main:
-        for name in ("gqa70b", "long_splitk", "fork_cow"):
+        for name in ("gqa70b", "long_splitk", "fork_cow", "tiny_fp32"):
             if name == args.workload:
                 continue
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
