@@ -83,6 +83,23 @@ def measured_traffic(workload: str, per_launch_alg: int):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_step_us(cfg, step, steps: int = 50) -> float:
+    """Host time of one decode step's table work (the slot mapping of every sequence's next
+    token, new blocks, the kernels' table and length arrays) with the array-held batch, on
+    this workload's batch: mean over `steps` steps."""
+    from paged_kv_cache_148_amd.block_manager import BlockManager, DecodeBatch
+    ctx = step.context_lens.astype(np.int64)
+    bm = BlockManager(int(sum(-(-int(c) // cfg.block_size) for c in ctx)) + len(ctx) * (steps // cfg.block_size + 2),
+                      cfg.block_size)
+    db = DecodeBatch(bm, [bm.new_sequence(int(c)) for c in ctx])
+    t = time.perf_counter()
+    for _ in range(steps):
+        db.step()
+        db.block_tables()
+        db.context_lens()
+    return (time.perf_counter() - t) / steps * 1e6
+
+
 def block_stats(cfg, step) -> dict:
     """Internal fragmentation of the step's block allocation (slots allocated but past the
     context, over all allocated slots) and block-table length."""
@@ -195,6 +212,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
         "copy_pairs": int(n_pairs), "path": binding.attention_path(cfg.num_heads, cfg.num_kv_heads, cfg.head_dim,
                                                                     cfg.block_size, 1 if bf16 else 0),
         "input_gen_s": gen_s,
+        "host_step_us": host_step_us(cfg, step),
         **block_stats(cfg, step),
     }
     if name == "fork_cow":
@@ -352,6 +370,7 @@ def main():
                    "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
         "seqs_per_s": round(res["seqs_per_s"], 1),
+        "host_step_us": round(res["host_step_us"], 1),
         "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {
             "bound": "hbm",

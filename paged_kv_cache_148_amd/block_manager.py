@@ -177,6 +177,107 @@ class BlockManager:
             raise AssertionError("free stack and zero refcounts disagree")
 
 
+class DecodeBatch:
+    """The running batch of a decode loop held as arrays, so that a step's host work -- every
+    sequence gains its newest token, takes a block when that token starts one, copies a shared
+    block before writing into it, and the slot mapping of the new tokens -- is a few array
+    operations rather than a loop over sequences (page "nano-vLLM . Ch04 . PagedAttention",
+    section 4: the slot mapping is built on the CPU once per batch; section 9: no Python per
+    token while the GPU runs the step).
+
+    ``tables`` [S, capacity] int32 rows (zeros past each row's ``nblocks``), ``lengths`` [S].
+    ``step()`` gives exactly what BlockManager.append_token then prepare_write would give,
+    sequence by sequence: a sequence whose new token starts a block takes the top of the free
+    stack, in sequence order; a write into a block shared with another sequence (after a fork)
+    takes the manager's per-sequence copy-on-write rules for that step.
+    """
+
+    def __init__(self, bm: BlockManager, seqs, capacity: int = 0):
+        self.bm = bm
+        self.lengths = np.array([s.length for s in seqs], dtype=np.int64)
+        self.nblocks = np.array([len(s.table) for s in seqs], dtype=np.int64)
+        width = max(int(self.nblocks.max(initial=0)) + 1, capacity)
+        self.tables = np.zeros((len(seqs), width), dtype=np.int32)
+        for i, s in enumerate(seqs):
+            self.tables[i, :len(s.table)] = s.table
+        self._rows = np.arange(len(seqs))
+
+    def _ensure(self, cols: int) -> None:
+        if cols > self.tables.shape[1]:
+            grown = np.zeros((self.tables.shape[0], max(cols, 2 * self.tables.shape[1])), dtype=np.int32)
+            grown[:, :self.tables.shape[1]] = self.tables
+            self.tables = grown
+
+    def block_tables(self) -> np.ndarray:
+        """int32 [S, max blocks] view of the tables (the kernels' block_tables)."""
+        return self.tables[:, :max(1, int(self.nblocks.max(initial=1)))]
+
+    def context_lens(self) -> np.ndarray:
+        return self.lengths.astype(np.int32)
+
+    def sequences(self) -> list:
+        return [Sequence(self.tables[i, :n].tolist(), int(l))
+                for i, (n, l) in enumerate(zip(self.nblocks.tolist(), self.lengths.tolist()))]
+
+    def step(self):
+        """One decode step.  Returns ``(slot_mapping, copy_pairs)`` (int64 [S] and [P, 2]), or
+        None -- changing nothing -- when the pool cannot supply the step's blocks."""
+        bm, B = self.bm, self.bm.block_size
+        pos = self.lengths                      # the new tokens' positions
+        col = pos // B
+        fresh = col >= self.nblocks             # the token starts a block the table lacks
+        keep = np.nonzero(~fresh)[0]
+        targets = self.tables[keep, col[keep]]
+        if (bm._ref[targets] > 1).any():
+            out = self._step_each(pos, col, fresh)
+        else:
+            idx = np.nonzero(fresh)[0]
+            if len(idx) > bm.num_free():
+                return None
+            if len(idx):
+                ids = bm.allocate(len(idx))     # the stack's top len(idx), bottom to top:
+                self._ensure(int(col[idx].max()) + 1)
+                self.tables[idx, col[idx]] = ids[::-1]   # one at a time, the top goes first
+                self.nblocks[idx] += 1
+            slots = self.tables[self._rows, col].astype(np.int64) * B + pos % B
+            out = slots, np.zeros((0, 2), dtype=np.int64)
+        if out is not None:
+            self.lengths += 1
+        return out
+
+    def _step_each(self, pos, col, fresh):
+        """The step sequence by sequence, with copy-on-write (BlockManager.prepare_write's
+        rules: copy, drop the old block's count, write the copy; the last holder of a block
+        writes in place).  A dry run first counts the blocks it takes."""
+        bm, B = self.bm, self.bm.block_size
+        takes, ref = int(fresh.sum()), {}
+        for i in np.nonzero(~fresh)[0].tolist():
+            b = int(self.tables[i, col[i]])
+            r = ref.get(b, int(bm._ref[b]))
+            if r > 1:
+                takes += 1
+                ref[b] = r - 1
+        if takes > bm.num_free():
+            return None
+        self._ensure(int(col.max()) + 1)
+        slots = np.empty(len(pos), dtype=np.int64)
+        pairs = []
+        for i in range(len(pos)):
+            c = int(col[i])
+            if fresh[i]:
+                self.tables[i, c] = bm.allocate(1)[0]
+                self.nblocks[i] += 1
+            else:
+                old = int(self.tables[i, c])
+                if bm._ref[old] > 1:
+                    new = bm.allocate(1)[0]
+                    bm._ref[old] -= 1
+                    self.tables[i, c] = new
+                    pairs.append((old, new))
+            slots[i] = int(self.tables[i, c]) * B + int(pos[i]) % B
+        return slots, np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+
+
 class PrefixCache:
     """Reuse of full prompt blocks across requests (page "PagedAttention", PidokuInfra topic
     10, section 5 "The relationship to prefix caching": hash the token ids of each block,
