@@ -169,6 +169,20 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / steps
+    # the same step captured once in a HIP graph and replayed (the calls allocate and clear
+    # nothing, and the queue counters return to zero inside each attention call)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_step_s = (time.perf_counter() - t0) / steps
+    del graph
     # The attention call's launch duration: the same call `steps` times back to back between one
     # pair of events on the launch stream.
     b2b = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -198,7 +212,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     nb = algorithmic_bytes(cfg, step)
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
-        "us_per_step": step_s * 1e6, "attention_us_mean": attn_s * 1e6,
+        "us_per_step": step_s * 1e6, "us_per_step_graph": graph_step_s * 1e6, "attention_us_mean": attn_s * 1e6,
         "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3, "mall_flushed_per_launch": flush_mall,
         "attention_us_events_p10": attn_ms[len(attn_ms) // 10] * 1e3,
         "attention_us_events_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
@@ -333,7 +347,7 @@ def main():
         return
     res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
                             args.flush_mall)
-    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step, attention {res['attention_us_mean']:.1f} us, "
+    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step ({res['us_per_step_graph']:.1f} from a graph), attention {res['attention_us_mean']:.1f} us, "
           f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
     del wl
@@ -345,7 +359,7 @@ def main():
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
                 r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
                 others[f"{name}/{w}" if name == "fork_cow" else name] = r
-                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step, attention {r['attention_us_mean']:.1f} us,"
+                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph), attention {r['attention_us_mean']:.1f} us,"
                       f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     cfg = workloads.CONFIGS[args.workload]
@@ -369,6 +383,7 @@ def main():
                    "block_size": res["block_size"], "partition_size": main_part, "sum_ctx": res["sum_ctx"],
                    "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
+        "us_per_step_graph": round(res["us_per_step_graph"], 2),
         "seqs_per_s": round(res["seqs_per_s"], 1),
         "host_step_us": round(res["host_step_us"], 1),
         "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),

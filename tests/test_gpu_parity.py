@@ -623,3 +623,58 @@ def test_large_batch_uses_fallback_grid():
         _, _, _, ref = H.oracle_step(wl, "steady", P, items=items)
         got = H.bits(d["out"]).reshape(cfg.num_seqs * cfg.num_heads, -1)[items]
         H.check_close(got, ref, "bf16", f"fallback P={P}")
+
+
+# ---------------------------------------------------------------------------
+# the decode step replayed from a HIP graph
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,num_seqs,P,which", [("mha7b", 8, 0, "steady"), ("gqa70b", 16, 512, "steady"),
+                                                   ("fork_cow", None, 512, "fork"), ("tiny_fp32", None, 8, "steady")])
+def test_decode_step_replays_from_a_hip_graph(name, num_seqs, P, which):
+    # copy_blocks -> paged_kv_write -> paged_attention_decode captured once and replayed: the calls
+    # allocate and clear nothing, and each attention call leaves its queue counters at zero, so
+    # every replay -- with eager calls on the same workspace and torch's own kernels in between --
+    # gives the eager step's caches and output bit for bit
+    import torch
+    wl = _wl(name, num_seqs=num_seqs)
+    cfg = wl.cfg
+    step = pbatch.step_for(wl, which)
+    ws = torch.zeros(binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim,
+                                                      step.max_context_len, P), dtype=torch.uint8, device="cuda")
+
+    def run(d, out):
+        if step.copy_pairs.shape[0]:
+            binding.copy_blocks(d["k_cache"], d["v_cache"], d["copy_pairs"])
+        binding.paged_kv_write(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+        binding.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                       d["context_lens"], step.max_context_len, wl.scale, P, ws)
+
+    _say("graph eager", name, which, "P", P)
+    d = H.upload(wl, step)
+    run(d, d["out"])
+    torch.cuda.synchronize()
+    want_out, want_k, want_v = H.bits(d["out"]).copy(), H.bits(d["k_cache"]).copy(), H.bits(d["v_cache"]).copy()
+    _, _, _, ref = H.oracle_step(wl, which, P)
+    H.check_close(want_out, ref, cfg.dtype, f"graph eager {name}")
+
+    g = H.upload(wl, step)
+    other = torch.empty_like(g["out"])
+    graph = torch.cuda.CUDAGraph()
+    _say("graph capture", name)
+    with torch.cuda.graph(graph):
+        run(g, g["out"])
+    for rep in range(4):
+        _say("graph replay", name, rep)
+        g["out"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert H.bits(g["out"]).tobytes() == want_out.tobytes(), f"replay {rep}: output"
+        assert H.bits(g["k_cache"]).tobytes() == want_k.tobytes(), f"replay {rep}: k_cache"
+        assert H.bits(g["v_cache"]).tobytes() == want_v.tobytes(), f"replay {rep}: v_cache"
+        assert not ws[:8].any().item(), f"replay {rep}: queue counters"
+        # eager work between replays: the same step on the same workspace into another buffer
+        run(g, other)
+        torch.cuda.synchronize()
+        assert H.bits(other).tobytes() == want_out.tobytes(), f"eager after replay {rep}"
