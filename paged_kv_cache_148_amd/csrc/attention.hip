@@ -48,7 +48,15 @@ namespace pkv {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTileDepth = 4;          // tile path: tiles per wave in the load ring (NB - 1 ahead)
+// Tile path: tiles per wave in the load ring (NB - 1 ahead).  A wave's tiles of an item are
+// rounded up to a multiple of NB with empty tiles, whose slots carry no bytes at the item's
+// end; one tile ahead per wave already keeps the memory system saturated and wastes the
+// fewest slots.  The deep ring hides an item's merge and partial-state stores behind more
+// loads in flight, which pays when items are short partitions (at most 512 tokens: 8 tiles
+// per wave), whose lengths are also whole multiples of the ring.
+constexpr int kTileDepthShallow = 2;
+constexpr int kTileDepthDeep = 4;
+constexpr int64_t kDeepRingMaxPartition = 512;
 constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
 constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
 constexpr int kClasses = 16;            // length classes of the longest-first schedule
@@ -665,6 +673,7 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
 template <int B, int NB, bool HM, bool MF>
 __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
+  static_assert(NB >= 2, "the ring holds the tile being computed and at least one ahead");
   constexpr int D = 128;
   __shared__ TileSmem sm;
   __shared__ LptSmem sched_sm;
@@ -1491,32 +1500,37 @@ static Pass1Fn vec_fn(int g, int B) {
   }
 }
 
-template <bool MF>
+template <bool MF, int NB>
 static Pass1Fn tile_fn(int B) {
   switch (B) {
-    case 4: return attn_tile_kernel<4, kTileDepth, false, MF>;
-    case 8: return attn_tile_kernel<8, kTileDepth, false, MF>;
-    case 16: return attn_tile_kernel<16, kTileDepth, false, MF>;
-    case 32: return attn_tile_kernel<32, kTileDepth, false, MF>;
-    case 64: return attn_tile_kernel<64, kTileDepth, false, MF>;
-    default: return attn_tile_kernel<128, kTileDepth, false, MF>;
+    case 4: return attn_tile_kernel<4, NB, false, MF>;
+    case 8: return attn_tile_kernel<8, NB, false, MF>;
+    case 16: return attn_tile_kernel<16, NB, false, MF>;
+    case 32: return attn_tile_kernel<32, NB, false, MF>;
+    case 64: return attn_tile_kernel<64, NB, false, MF>;
+    default: return attn_tile_kernel<128, NB, false, MF>;
   }
 }
 
-template <bool MF>
+template <bool MF, int NB>
 static Pass1Fn tile_hm_fn(int B) {
   switch (B) {
-    case 16: return attn_tile_kernel<16, kTileDepth, true, MF>;
-    case 32: return attn_tile_kernel<32, kTileDepth, true, MF>;
-    case 64: return attn_tile_kernel<64, kTileDepth, true, MF>;
-    default: return attn_tile_kernel<128, kTileDepth, true, MF>;
+    case 16: return attn_tile_kernel<16, NB, true, MF>;
+    case 32: return attn_tile_kernel<32, NB, true, MF>;
+    case 64: return attn_tile_kernel<64, NB, true, MF>;
+    default: return attn_tile_kernel<128, NB, true, MF>;
   }
 }
 
-static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major) {
-  if (head_major) return path == PKV_PATH_TILE_VALU ? tile_hm_fn<false>(B) : tile_hm_fn<true>(B);
-  if (path == PKV_PATH_MFMA) return tile_fn<true>(B);
-  if (path == PKV_PATH_TILE_VALU) return tile_fn<false>(B);
+// deep: the MFMA tiles' deep load ring (split into partitions of at most 512 tokens).  One
+// query head per KV head keeps the shallow ring: its merge and stores are a single head's.
+static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major, bool deep) {
+  if (head_major) {
+    if (path == PKV_PATH_TILE_VALU) return tile_hm_fn<false, kTileDepthShallow>(B);
+    return deep ? tile_hm_fn<true, kTileDepthDeep>(B) : tile_hm_fn<true, kTileDepthShallow>(B);
+  }
+  if (path == PKV_PATH_MFMA) return deep ? tile_fn<true, kTileDepthDeep>(B) : tile_fn<true, kTileDepthShallow>(B);
+  if (path == PKV_PATH_TILE_VALU) return tile_fn<false, kTileDepthShallow>(B);
   if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
   return D == 128 ? vec_fn<float, 128>(g, B) : vec_fn<float, 64>(g, B);
 }
@@ -1626,7 +1640,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const bool bf16 = dtype == PKV_DTYPE_BF16;
-  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major);
+  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, np > 1 && P <= kDeepRingMaxPartition);
   // persistent workgroups when the schedule fits in LDS, else one workgroup per possible item
   size_t dyn_lds = 0;
   int64_t grid = items;

@@ -204,6 +204,7 @@ SHAPES = [
     ("bf16", 5, 32, 4, 128, 64, (1, 700)),    # B = 64, g = 8
     ("bf16", 4, 8, 8, 128, 128, (1, 900)),    # B = 128, g = 1
     ("bf16", 3, 16, 2, 128, 128, (1, 2600)),  # B = 128, g = 8, more than 64 tiles per wave
+    ("bf16", 3, 8, 2, 128, 8, (2000, 5000)),  # MFMA, B = 8, long: the shallow ring's split partitions
     ("f32", 4, 8, 8, 128, 16, (1, 200)),      # fp32, D = 128 (32 lanes per row)
     ("f32", 4, 8, 2, 64, 8, (1, 200)),        # fp32 GQA on the vector path
     ("f32", 3, 5, 5, 64, 32, (1, 200)),
@@ -216,8 +217,9 @@ def test_shape_sweep_parity(shape):
     cfg = workloads.Config("sweep", dt, S, Hq, Hkv, D, B, ("uniform", lo, hi), seed=100 + Hq + D + B)
     wl = workloads.make_workload(cfg)
     step = pbatch.step_for(wl)
-    # below 16 slots per block also a partition that is not a multiple of the 16-token tile
-    for P in (0, 4 * B if B >= 16 else 64) + ((3 * B,) if B < 16 else ()):
+    # below 16 slots per block also a partition that is not a multiple of the 16-token tile;
+    # long contexts also split into partitions above 512 tokens (the shallow load ring)
+    for P in (0, 4 * B if B >= 16 else 64) + ((3 * B,) if B < 16 else ()) + ((1024,) if hi > 2048 else ()):
         _say("sweep", shape, "P", P)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P)
@@ -396,8 +398,8 @@ HM_SHAPES = [
     (4, 8, 8, 16, (1, 600), (0, 128)),      # g = 1
     (4, 24, 8, 32, (1, 500), (0, 96)),      # g = 3, B = 32
     (3, 16, 4, 128, (1, 1500), (0, 256)),   # g = 4, B = 128
-    (3, 8, 2, 64, (4200, 9000), (0, 512)),  # more than 64 tiles per wave
-    (3, 4, 4, 128, (4200, 9000), (0, 512)), # g = 1 (VALU tiles), more than 64 tiles per wave
+    (3, 8, 2, 64, (4200, 9000), (0, 512, 1024)),  # more than 64 tiles per wave; both load rings
+    (3, 4, 4, 128, (4200, 9000), (0, 512, 1024)), # g = 1 (VALU tiles), more than 64 tiles per wave
 ]
 
 
