@@ -258,6 +258,51 @@ def copy_probe(reps: int = 3) -> None:
                       "bytes_written_per_call": nbytes}), flush=True)
 
 
+def movers(steps: int = 20) -> None:
+    """paged_kv_write and copy_blocks at sizes where HBM bandwidth, not launch latency, bounds
+    them (the decode configurations write and copy well under 1 MB per step).  Pool of 16384
+    blocks of 16 slots, 8 KV heads, head_dim 128, bf16 (32 KiB per block per tensor): a write of
+    131072 tokens to distinct slots scattered over the pool (256 MiB of K and V each way), and a
+    copy of 8192 (src, dst) block pairs (also 256 MiB each way).  One pair of HIP events around
+    `steps` back-to-back calls on the launch stream."""
+    import torch
+    from paged_kv_cache_148_amd import binding
+    N, B, Hkv, D = 16384, 16, 8, 128
+    g = torch.Generator().manual_seed(7)
+    kc = torch.zeros(N, B, Hkv, D, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    T = N * B // 2
+    kn = torch.randn(T, Hkv, D, generator=g).to(torch.bfloat16).cuda()
+    vn = torch.randn(T, Hkv, D, generator=g).to(torch.bfloat16).cuda()
+    slots = torch.randperm(N * B, generator=g)[:T].to(torch.int64).cuda()
+    perm = torch.randperm(N, generator=g)
+    pairs = torch.stack([perm[: N // 2], perm[N // 2:]], dim=1).to(torch.int64).cuda()
+    row = Hkv * D * 2
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / steps
+
+    res = {}
+    for name, call, nbytes in (
+            ("paged_kv_write", lambda: binding.paged_kv_write(kn, vn, kc, vc, slots), 2 * (2 * T * row) + 8 * T),
+            ("copy_blocks", lambda: binding.copy_blocks(kc, vc, pairs), 2 * (2 * (N // 2) * B * row) + 16 * (N // 2))):
+        t = timed(call)
+        res[name] = {"us": round(t * 1e6, 2), "algorithmic_bytes": nbytes, "GB/s": round(nbytes / t / 1e9, 1),
+                     "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] {name}: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
+    print(json.dumps({"movers": res, "tokens_written": T, "pairs_copied": N // 2, "steps": steps,
+                      "timing": f"HIP events around {steps} back-to-back calls on the launch stream",
+                      "kernel_source_hash": kernel_source_hash()}), flush=True)
+
+
 def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
     """The CPU oracle on the same inputs: whole-step passes (copies, write, attention) on all
     host cores, repeated until about budget_s seconds have been spent."""
@@ -303,6 +348,8 @@ def main():
     ap.add_argument("--partition", type=int, default=None)
     ap.add_argument("--only-main", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--movers", action="store_true",
+                    help="only time paged_kv_write and copy_blocks at HBM-bound sizes (256 MiB each way)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
     ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous", "head_major"],
@@ -325,6 +372,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.movers:
+        movers()
         return
 
     main_part = PARTITION[args.workload] if args.partition is None else args.partition
