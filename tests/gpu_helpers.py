@@ -74,5 +74,6 @@ def check_close(gpu_bits, ref, dtype: str, what: str = ""):
         ok = bool((err <= F32_ABS + F32_REL * np.abs(ref)).all())
     else:
         ok = max_abs <= BF16_MAX_ABS
+    print(f"[parity] {what}: n={err.size} max_abs={max_abs:.3e} max_rel={max_rel:.3e}", flush=True)
     assert np.isfinite(g).all() and ok, f"{what}: max_abs={max_abs:.3e} max_rel={max_rel:.3e}"
     return max_abs, max_rel
