@@ -365,9 +365,103 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// The same schedule for at most 64 sequences: one wave holds every length in a lane and
+// builds it in registers (class counts by ballot, the class starts by one scan), with a single
+// barrier in all.
+__device__ LptSched build_lpt_schedule_one_wave(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order,
+                                                LptSmem &ss) {
+  const int S = a.S, lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    const bool valid = lane < S;
+    const int c = valid ? a.ctx[lane] : 0;
+    int nfull, cls;
+    classify(a, c, valid, nfull, cls);
+    const int incl = wave_incl_scan(nfull);
+    uint64_t mine = 0ull;
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) {
+      const uint64_t m = __ballot(cls == k);
+      if (lane == k) cnt = __popcll(m);
+      if (cls == k) mine = m;
+    }
+    const int cincl = wave_incl_scan(cnt);   // lanes 0 .. kClasses - 1: classes; others count 0
+    const int start = __shfl(cincl - cnt, cls < kClasses ? cls : 0);
+    if (valid) {
+      sm_ctx[lane] = c;
+      sm_pref[lane] = incl;
+      sm_order[start + __popcll(mine & ((1ull << lane) - 1ull))] = lane;
+    }
+    if (lane == 63) ss.total_full = incl;
+  }
+  __syncthreads();
+  LptSched r;
+  r.total_full = min(max(ss.total_full, 0), S * a.Hkv * (a.max_parts - 1));
+  r.total = r.total_full + S * a.Hkv;
+  return r;
+}
+
+// The same schedule for 65 .. 256 sequences: wave w holds chunk w (sequences 64 w .. 64 w + 63)
+// in registers, publishes its class counts and full-partition count, and after one barrier
+// places its own sequences using the earlier chunks' counts; two barriers in all.
+__device__ LptSched build_lpt_schedule_four_waves(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order,
+                                                  LptSmem &ss) {
+  const int S = a.S, lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int Q = (S + 63) >> 6;
+  const int i = 64 * q + lane;
+  const bool valid = i < S;
+  const int c = valid ? a.ctx[i] : 0;
+  int nfull = 0, cls = kClasses, incl = 0, cnt = 0;
+  uint64_t mine = 0ull;
+  if (q < Q) {
+    classify(a, c, valid, nfull, cls);
+    incl = wave_incl_scan(nfull);
+#pragma unroll
+    for (int k = 0; k < kClasses; ++k) {
+      const uint64_t m = __ballot(cls == k);
+      if (lane == k) cnt = __popcll(m);
+      if (cls == k) mine = m;
+    }
+    if (lane < kClasses) ss.cnt[q][lane] = cnt;
+    if (lane == 63) ss.cfull[q] = incl;
+    if (valid) sm_ctx[i] = c;
+  }
+  __syncthreads();
+  int total_full = 0, full_before = 0;
+  for (int p = 0; p < Q; ++p) {
+    const int f = ss.cfull[p];
+    total_full += f;
+    if (p < q) full_before += f;
+  }
+  if (q < Q) {
+    // lane k: sequences of class k in the earlier chunks, and in all chunks
+    int before = 0, tot = 0;
+    if (lane < kClasses) {
+      for (int p = 0; p < Q; ++p) {
+        const int v = ss.cnt[p][lane];
+        tot += v;
+        if (p < q) before += v;
+      }
+    }
+    const int cincl = wave_incl_scan(tot);
+    const int start = __shfl(cincl - tot + before, cls < kClasses ? cls : 0);
+    if (valid) {
+      sm_pref[i] = incl + full_before;
+      sm_order[start + __popcll(mine & ((1ull << lane) - 1ull))] = i;
+    }
+  }
+  __syncthreads();
+  LptSched r;
+  r.total_full = min(max(total_full, 0), S * a.Hkv * (a.max_parts - 1));
+  r.total = r.total_full + S * a.Hkv;
+  return r;
+}
+
 // Builds the schedule; ends with a barrier.
 __device__ LptSched build_lpt_schedule(const AttnArgs &a, int *sm_pref, int *sm_ctx, int *sm_order, LptSmem &ss) {
   const int S = a.S, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (S <= 64) return build_lpt_schedule_one_wave(a, sm_pref, sm_ctx, sm_order, ss);
+  if (S <= 64 * kWaves) return build_lpt_schedule_four_waves(a, sm_pref, sm_ctx, sm_order, ss);
   const int Q = (S + 63) >> 6;
   constexpr int kPer = kMaxSchedSeqs / kThreads;
   {

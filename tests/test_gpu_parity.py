@@ -596,9 +596,10 @@ def test_work_queue_counters_return_to_zero(name, P):
     H.check_close(first, ref, cfg.dtype, f"queue {name}")
 
 
-@pytest.mark.parametrize("num_seqs", [300, 4096])
+@pytest.mark.parametrize("num_seqs", [40, 100, 200, 300, 4096])
 def test_persistent_schedule_many_sequences(num_seqs):
-    # the persistent path's longest-first schedule over many 64-sequence chunks, up to the most
+    # the persistent path's longest-first schedule: one wave (up to 64 sequences), one wave per
+    # 64-sequence chunk (up to 256, some waves without a chunk), and many chunks up to the most
     # sequences it stages in LDS: every item exactly once, with full and last partitions mixed
     cfg = workloads.Config("chunks", "bf16", num_seqs, 8, 2, 128, 16, ("uniform", 1, 400), seed=31 + num_seqs)
     wl = workloads.make_workload(cfg)
