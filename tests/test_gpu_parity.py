@@ -544,12 +544,15 @@ def test_full_size_sampled_parity(name):
 # device-side value handling (bounds checks in the kernels turn these into values)
 # ---------------------------------------------------------------------------
 
-def test_bad_device_values_give_defined_outputs():
+@pytest.mark.parametrize("num_seqs,P", [(4, 0), (4, 256), (100, 0), (300, 256)])
+def test_bad_device_values_give_defined_outputs(num_seqs, P):
+    # the three forms of the schedule build (one wave, a wave per chunk, many chunks), split or not
     import torch
-    wl = _wl("gqa70b", num_seqs=4)
+    wl = _wl("gqa70b", num_seqs=num_seqs)
     step = pbatch.step_for(wl)
+    _say("bad values", num_seqs, "P", P)
     d = H.upload(wl, step)
-    H.gpu_step(wl, step, d, 0)
+    H.gpu_step(wl, step, d, P)
     good = H.bits(d["out"]).copy()
     # seq 0: context 0 -> zeros; seq 1: a table entry outside the pool -> NaN;
     # seq 2: context above the host bound -> NaN; seq 3 unaffected
@@ -560,12 +563,12 @@ def test_bad_device_values_give_defined_outputs():
     bt[1, 0] = wl.num_blocks + 1000
     out = torch.empty_like(d["out"])
     binding.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], bt, ctx, step.max_context_len,
-                                   wl.scale, 0)
+                                   wl.scale, P)
     torch.cuda.synchronize()
     o = H.widen(H.bits(out))
     assert (o[0] == 0).all()
     assert np.isnan(o[1]).all() and np.isnan(o[2]).all()
-    assert H.bits(out)[3].tobytes() == good[3].tobytes()
+    assert H.bits(out)[3:].tobytes() == good[3:].tobytes()
 
 
 # ---------------------------------------------------------------------------
