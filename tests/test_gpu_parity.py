@@ -599,6 +599,31 @@ def test_work_queue_counters_return_to_zero(name, P):
     H.check_close(first, ref, cfg.dtype, f"queue {name}")
 
 
+@pytest.mark.parametrize("name,P", [("mha7b", 0), ("gqa70b", 512)])
+def test_back_to_back_calls_share_a_workspace(name, P):
+    # calls queued on one stream with no synchronization between them, on one workspace: each
+    # starts after the one before has finished and reset the queue counters, so every output
+    # equals the output of a lone call
+    import torch
+    wl = _wl(name, num_seqs=24)
+    step = pbatch.step_for(wl)
+    cfg = wl.cfg
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P)
+    want = H.bits(d["out"]).copy()
+    ws = torch.zeros(binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim,
+                                                      step.max_context_len, P), dtype=torch.uint8, device="cuda")
+    outs = [torch.full_like(d["out"], float("nan")) for _ in range(6)]
+    _say("back to back", name, "P", P)
+    for o in outs:
+        binding.paged_attention_decode(o, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                       d["context_lens"], step.max_context_len, wl.scale, P, ws)
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert H.bits(o).tobytes() == want.tobytes(), f"call {i}"
+    assert not ws[:8].any().item()
+
+
 @pytest.mark.parametrize("num_seqs", [40, 100, 200, 300, 4096])
 def test_persistent_schedule_many_sequences(num_seqs):
     # the persistent path's longest-first schedule: one wave (up to 64 sequences), one wave per
