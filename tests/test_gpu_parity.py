@@ -624,6 +624,36 @@ def test_back_to_back_calls_share_a_workspace(name, P):
     assert not ws[:8].any().item()
 
 
+def test_two_streams_with_their_own_workspaces():
+    # two decode steps in flight at once on two streams (default priority), each with its own
+    # pool, output and workspace: the persistent launches share the CUs and nothing else
+    import torch
+    cases = []
+    for name, P in (("mha7b", 0), ("gqa70b", 512)):
+        wl = _wl(name, num_seqs=16)
+        step = pbatch.step_for(wl)
+        cfg = wl.cfg
+        d = H.upload(wl, step)
+        ws = torch.zeros(binding.attention_workspace_size(cfg.num_seqs, cfg.num_heads, cfg.head_dim,
+                                                          step.max_context_len, P), dtype=torch.uint8, device="cuda")
+        cases.append((wl, step, d, ws, P))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    _say("two streams")
+    for (wl, step, d, ws, P), st in zip(cases, streams):
+        with torch.cuda.stream(st):
+            binding.paged_kv_write(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
+            for _ in range(3):
+                binding.paged_attention_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                               d["context_lens"], step.max_context_len, wl.scale, P, ws)
+    torch.cuda.synchronize()
+    for wl, step, d, ws, P in cases:
+        _, kc, _, ref = H.oracle_step(wl, "steady", P)
+        assert H.bits(d["k_cache"]).tobytes() == kc.tobytes()
+        H.check_close(H.bits(d["out"]), ref, wl.cfg.dtype, f"two streams {wl.cfg.name}")
+        assert not ws[:8].any().item()
+
+
 @pytest.mark.parametrize("num_seqs", [40, 100, 200, 300, 4096])
 def test_persistent_schedule_many_sequences(num_seqs):
     # the persistent path's longest-first schedule: one wave (up to 64 sequences), one wave per
