@@ -258,7 +258,7 @@ def copy_probe(reps: int = 3) -> None:
                       "bytes_written_per_call": nbytes}), flush=True)
 
 
-def movers(steps: int = 20) -> None:
+def movers(steps: int = 20) -> dict:
     """paged_kv_write and copy_blocks at sizes where HBM bandwidth, not launch latency, bounds
     them (the decode configurations write and copy well under 1 MB per step).  Pool of 16384
     blocks of 16 slots, 8 KV heads, head_dim 128, bf16 (32 KiB per block per tensor): a write of
@@ -298,9 +298,10 @@ def movers(steps: int = 20) -> None:
         res[name] = {"us": round(t * 1e6, 2), "algorithmic_bytes": nbytes, "GB/s": round(nbytes / t / 1e9, 1),
                      "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] {name}: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
-    print(json.dumps({"movers": res, "tokens_written": T, "pairs_copied": N // 2, "steps": steps,
-                      "timing": f"HIP events around {steps} back-to-back calls on the launch stream",
-                      "kernel_source_hash": kernel_source_hash()}), flush=True)
+    del kc, vc, kn, vn, slots, pairs
+    torch.cuda.empty_cache()
+    return {"results": res, "tokens_written": T, "pairs_copied": N // 2, "steps": steps,
+            "timing": f"HIP events around {steps} back-to-back calls on the launch stream"}
 
 
 def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
@@ -374,7 +375,7 @@ def main():
         copy_probe()
         return
     if args.movers:
-        movers()
+        print(json.dumps({"movers": movers(), "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
 
     main_part = PARTITION[args.workload] if args.partition is None else args.partition
@@ -412,6 +413,8 @@ def main():
                 print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph), attention {r['attention_us_mean']:.1f} us,"
                       f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # paged_kv_write and copy_blocks where HBM, not launch latency, bounds them
+    mv = None if args.only_main else movers()
     cfg = workloads.CONFIGS[args.workload]
     nb = res["bytes"]
     traffic = measured_traffic(args.workload, nb["attention"])
@@ -456,6 +459,7 @@ def main():
         "cpu_baseline": cpu,
         "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in others.items()},
+        "movers": mv,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
