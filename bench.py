@@ -59,12 +59,16 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", "", text)
 
 
+# the sources the attention kernels are compiled from (the counter records describe them)
+ATTENTION_SOURCES = ("attention.hip", "pkv_device.h")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the code of paged_kv_cache_148_amd/csrc/* (comments and whitespace removed),
-    first 16 hex digits: the key of the committed counter records."""
+    """sha256 over the code of the attention kernels' sources (comments and whitespace
+    removed), first 16 hex digits: the key of the committed counter records."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_148_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTENTION_SOURCES:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
@@ -304,6 +308,32 @@ def movers(steps: int = 20) -> dict:
             "timing": f"HIP events around {steps} back-to-back calls on the launch stream"}
 
 
+def stream_read_ceiling(steps: int = 20, gib: int = 2) -> dict:
+    """A plain streaming read of `gib` GiB (16-byte non-temporal loads, no indirection, no
+    arithmetic): what this machine's HBM delivers to a read-only kernel, the context for the
+    decode kernels' bandwidth.  One pair of HIP events around `steps` back-to-back reads."""
+    import torch
+    from paged_kv_cache_148_amd import binding
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        binding.stream_read_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        binding.stream_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = gib << 30
+    del buf, sink
+    torch.cuda.empty_cache()
+    print(f"[bench] streaming read of {gib} GiB: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr,
+          flush=True)
+    return {"bytes": nbytes, "us": round(t * 1e6, 2), "GB/s": round(nbytes / t / 1e9, 1),
+            "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
     """The CPU oracle on the same inputs: whole-step passes (copies, write, attention) on all
     host cores, repeated until about budget_s seconds have been spent."""
@@ -413,8 +443,9 @@ def main():
                 print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph), attention {r['attention_us_mean']:.1f} us,"
                       f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
-    # paged_kv_write and copy_blocks where HBM, not launch latency, bounds them
+    # paged_kv_write and copy_blocks where HBM, not launch latency, bounds them; a plain read
     mv = None if args.only_main else movers()
+    rd = None if args.only_main else stream_read_ceiling()
     cfg = workloads.CONFIGS[args.workload]
     nb = res["bytes"]
     traffic = measured_traffic(args.workload, nb["attention"])
@@ -455,11 +486,13 @@ def main():
             "launch_us_mean": round(res["attention_us_mean"], 2),
             "timing": f"HIP events around {args.steps} back-to-back attention launches on the launch stream",
             "launch_us_events_each": round(res["attention_us_events_mean"], 2),
+            "frac_of_stream_read": round(res["attention_alg_gbs"] / rd["GB/s"], 4) if rd else None,
         },
         "cpu_baseline": cpu,
         "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                       for k, v in others.items()},
         "movers": mv,
+        "stream_read": rd,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

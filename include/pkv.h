@@ -191,6 +191,17 @@ pkv_status paged_attention_decode_head_major(void *out, const void *q, const voi
 pkv_path pkv_attention_path_head_major(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                        int32_t block_size, pkv_dtype dtype);
 
+/*
+ * pkv_stream_read_probe -- measurement only, not part of the decode path: one plain streaming
+ * read of `bytes` of device memory at `buf` (16-byte aligned; a whole number of 16-byte words
+ * is read, the rest ignored) with non-temporal 16-byte loads, to time the rate this device's
+ * HBM delivers to a read-only kernel without indirection.  `sink` is a caller-owned device word
+ * that the kernel may write (it folds what it reads so that no load is dead); its value means
+ * nothing.  PKV_ERR_INVALID_ARG for null or misaligned pointers or bytes < 16; asynchronous on
+ * `stream`, like every call here.
+ */
+pkv_status pkv_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *pkv_status_string(pkv_status status);
 

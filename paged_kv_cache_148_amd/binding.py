@@ -20,7 +20,7 @@ PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA, PKV_PATH_TILE_VALU = 0, 1, 2, 3
 # every symbol include/pkv.h declares
 EXPORTS = ("paged_kv_write", "paged_attention_decode", "copy_blocks", "pkv_attention_workspace_size",
            "pkv_attention_path", "pkv_status_string", "paged_kv_write_head_major",
-           "paged_attention_decode_head_major", "pkv_attention_path_head_major")
+           "paged_attention_decode_head_major", "pkv_attention_path_head_major", "pkv_stream_read_probe")
 
 _lib = None
 
@@ -64,6 +64,8 @@ def lib():
         L.copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i32, ctypes.c_int, p]
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_status_string.argtypes = [ctypes.c_int]
+        L.pkv_stream_read_probe.restype = ctypes.c_int
+        L.pkv_stream_read_probe.argtypes = [p, sz, p, p]
         _lib = L
     return _lib
 
@@ -239,3 +241,15 @@ def paged_attention_decode_head_major(out, q, k_cache, v_cache, block_tables, co
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q, stream))
     _check(st, "paged_attention_decode_head_major")
+
+
+def stream_read_probe(buf, sink, stream=None) -> None:
+    """Measurement only: one plain streaming read of the whole of `buf` (a GPU tensor), the
+    bandwidth reference for the decode kernels.  `sink` is a GPU int32 tensor of at least one
+    element that the kernel may write."""
+    torch = _torch()
+    if not buf.is_cuda or not sink.is_cuda or sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("stream_read_probe needs a GPU buffer and a GPU int32 sink")
+    st = lib().pkv_stream_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                     ctypes.c_void_p(sink.data_ptr()), _stream(buf, stream))
+    _check(st, "pkv_stream_read_probe")

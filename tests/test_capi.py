@@ -146,3 +146,13 @@ def test_binding_refuses_cpu_tensors(L):
     k = torch.zeros(4, 16, 2, 64)
     with pytest.raises(ValueError):
         paged_kv_write(torch.zeros(1, 2, 64), torch.zeros(1, 2, 64), k, k.clone(), torch.zeros(1, dtype=torch.int64))
+
+
+def test_stream_read_probe_rejects_bad_arguments(L):
+    sink = ctypes.c_void_p(256)   # never dereferenced: every call below fails its host checks
+    buf = ctypes.c_void_p(4096)
+    assert L.pkv_stream_read_probe(None, 1 << 20, sink, None) == PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read_probe(buf, 1 << 20, None, None) == PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read_probe(buf, 8, sink, None) == PKV_ERR_INVALID_ARG             # under one word
+    assert L.pkv_stream_read_probe(ctypes.c_void_p(4100), 1 << 20, sink, None) == PKV_ERR_INVALID_ARG
+    assert L.pkv_stream_read_probe(buf, 1 << 20, ctypes.c_void_p(258), None) == PKV_ERR_INVALID_ARG

@@ -739,3 +739,16 @@ def test_decode_step_replays_from_a_hip_graph(name, num_seqs, P, which):
         run(g, other)
         torch.cuda.synchronize()
         assert H.bits(other).tobytes() == want_out.tobytes(), f"eager after replay {rep}"
+
+
+def test_stream_read_probe_runs():
+    # the measurement-only read: it runs over a buffer that is not a multiple of its loop's
+    # stride and of 16 bytes, and leaves the buffer as it was
+    import torch
+    buf = torch.arange((3 << 20) + 5, dtype=torch.int32, device="cuda").view(torch.uint8)[: (12 << 20) + 7]
+    before = buf.clone()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    binding.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
+
