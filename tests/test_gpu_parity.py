@@ -654,6 +654,49 @@ def test_two_streams_with_their_own_workspaces():
         assert not ws[:8].any().item()
 
 
+@pytest.mark.parametrize("name,num_seqs,which,P", [("fork_cow", None, "fork", 512), ("mha7b", 6, "steady", 0)])
+def test_pool_beyond_4_gib(name, num_seqs, which, P):
+    # every block the step touches lies past the first 4 GiB of a pool of more than 4 GiB per
+    # tensor (the oracle's pool holds the same blocks under their own ids, which relabelling does
+    # not change): slots, copies and table entries address it with 64-bit offsets
+    import torch
+    wl = _wl(name, num_seqs=num_seqs)
+    step = pbatch.step_for(wl, which)
+    cfg = wl.cfg
+    n_small = wl.num_blocks
+    block_bytes = cfg.block_size * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    first = -(-(4 << 30) // block_bytes)            # first block wholly past 4 GiB
+    span = 1 << max(10, (n_small - 1).bit_length())
+    n_big = first + span
+    new_id = first + (np.arange(n_small, dtype=np.int64) * 7) % span   # distinct, scattered
+    _say("pool beyond 4 GiB", name, "blocks", n_big, "bytes per tensor", n_big * block_bytes)
+    big = {}
+    for key in ("k_cache", "v_cache"):
+        t = torch.empty((n_big,) + tuple(wl.k_cache.shape[1:]), dtype=torch.bfloat16, device="cuda")
+        t[torch.from_numpy(new_id).cuda()] = pbatch.to_torch(getattr(wl, key), "cuda", True)
+        big[key] = t
+    d = H.upload(wl, step)
+    del d["k_cache"], d["v_cache"]
+    B = cfg.block_size
+    slots = step.slot_mapping.astype(np.int64)
+    slots_big = new_id[slots // B] * B + slots % B
+    pairs_big = new_id[step.copy_pairs.astype(np.int64)].reshape(-1, 2) if step.copy_pairs.size else step.copy_pairs
+    tables_big = new_id[np.clip(step.block_tables.astype(np.int64), 0, n_small - 1)].astype(np.int32)
+    if pairs_big.size:
+        binding.copy_blocks(big["k_cache"], big["v_cache"], pbatch.to_torch(np.ascontiguousarray(pairs_big), "cuda"))
+    binding.paged_kv_write(d["k_new"], d["v_new"], big["k_cache"], big["v_cache"], pbatch.to_torch(slots_big, "cuda"))
+    binding.paged_attention_decode(d["out"], d["q"], big["k_cache"], big["v_cache"], pbatch.to_torch(tables_big, "cuda"),
+                                   d["context_lens"], step.max_context_len, wl.scale, P)
+    torch.cuda.synchronize()
+    _, kc, vc, ref = H.oracle_step(wl, which, P)
+    idx = torch.from_numpy(new_id).cuda()
+    assert H.bits(big["k_cache"][idx]).tobytes() == kc.tobytes()
+    assert H.bits(big["v_cache"][idx]).tobytes() == vc.tobytes()
+    H.check_close(H.bits(d["out"]), ref, cfg.dtype, f"beyond 4 GiB {name}")
+    del big
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("num_seqs", [40, 100, 200, 300, 4096])
 def test_persistent_schedule_many_sequences(num_seqs):
     # the persistent path's longest-first schedule: one wave (up to 64 sequences), one wave per
