@@ -187,6 +187,23 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     torch.cuda.synchronize()
     graph_step_s = (time.perf_counter() - t0) / steps
     del graph
+    # the same step through paged_attention_decode_write: the write rides in the attention
+    # launch on the tile paths (row layout)
+    fused_step_s = None
+    if not hm:
+        def fused_step():
+            if n_pairs:
+                copy(kc, vc, pairs)
+            binding.paged_attention_decode_write(out, q, kn, vn, kc, vc, tables, ctx, step.max_context_len, wl.scale,
+                                                 partition, ws)
+        for _ in range(warmup):
+            fused_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fused_step()
+        torch.cuda.synchronize()
+        fused_step_s = (time.perf_counter() - t0) / steps
     # The attention call's launch duration: the same call `steps` times back to back between one
     # pair of events on the launch stream.
     b2b = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -216,7 +233,8 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     nb = algorithmic_bytes(cfg, step)
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
-        "us_per_step": step_s * 1e6, "us_per_step_graph": graph_step_s * 1e6, "attention_us_mean": attn_s * 1e6,
+        "us_per_step": step_s * 1e6, "us_per_step_graph": graph_step_s * 1e6,
+        "us_per_step_fused": fused_step_s * 1e6 if fused_step_s else None, "attention_us_mean": attn_s * 1e6,
         "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3, "mall_flushed_per_launch": flush_mall,
         "attention_us_events_p10": attn_ms[len(attn_ms) // 10] * 1e3,
         "attention_us_events_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
@@ -428,7 +446,7 @@ def main():
         return
     res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
                             args.flush_mall)
-    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step ({res['us_per_step_graph']:.1f} from a graph), attention {res['attention_us_mean']:.1f} us, "
+    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step ({res['us_per_step_graph']:.1f} from a graph, {res['us_per_step_fused'] or 0:.1f} fused), attention {res['attention_us_mean']:.1f} us, "
           f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
     del wl
@@ -440,7 +458,7 @@ def main():
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
                 r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
                 others[f"{name}/{w}" if name == "fork_cow" else name] = r
-                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph), attention {r['attention_us_mean']:.1f} us,"
+                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph, {r['us_per_step_fused'] or 0:.1f} fused), attention {r['attention_us_mean']:.1f} us,"
                       f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
 
     # paged_kv_write and copy_blocks where HBM, not launch latency, bounds them; a plain read
@@ -468,6 +486,7 @@ def main():
                    "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
         "us_per_step_graph": round(res["us_per_step_graph"], 2),
+        "us_per_step_fused": round(res["us_per_step_fused"], 2) if res["us_per_step_fused"] else None,
         "seqs_per_s": round(res["seqs_per_s"], 1),
         "host_step_us": round(res["host_step_us"], 1),
         "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),

@@ -155,6 +155,35 @@ pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mappin
                        pkv_dtype dtype, void *stream);
 
 /*
+ * paged_attention_decode_write -- a decode step's write and attention in one launch: the
+ * same as paged_kv_write of k_new[s], v_new[s] ([num_seqs, num_kv_heads, head_dim]) to the
+ * slot of position context_lens[s] - 1 of each sequence (the slot its table gives:
+ * block_tables[s, (ctx - 1) / block_size] * block_size + (ctx - 1) % block_size), followed by
+ * paged_attention_decode over contexts that include that token (tokentrails steps 2-3: write
+ * the new token's K/V, then attend; nano-vLLM section 4 "Mechanism 3": the slot from the
+ * table).  Outputs and caches are bit-identical to those two calls.  On the tile paths
+ * (PKV_PATH_MFMA, PKV_PATH_TILE_VALU) the row of each sequence's new token is written by the
+ * work item that attends to it and used from registers, in the one launch; where the MFMA
+ * tiles split into partitions of at most 512 tokens, and on the vector path, the write is a
+ * launch of its own just before the attention's.
+ *
+ * Arguments as for paged_attention_decode, plus k_new and v_new (device, 16-byte aligned;
+ * null gives PKV_ERR_INVALID_ARG); k_cache and v_cache are written.  The row layout only
+ * (PKV_ERR_UNSUPPORTED for shapes paged_attention_decode does not take).  A sequence with
+ * context_lens[s] <= 0 or > max_context_len, or whose new token's table entry lies outside
+ * [0, num_blocks), writes nothing (and gets the outputs paged_attention_decode gives it).
+ * The slots written must be distinct and must not be shared with another sequence (after a
+ * fork, copy_blocks first), as for paged_kv_write.
+ */
+pkv_status paged_attention_decode_write(void *out, const void *q, const void *k_new, const void *v_new,
+                                        void *k_cache, void *v_cache, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                        int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, float scale, int32_t partition_size, void *workspace,
+                                        size_t workspace_bytes, pkv_dtype dtype, void *stream);
+
+/*
  * The head-major cache layout (PidokuInfra page, section 5 "The layout, more precisely"):
  *   k_cache : [num_blocks, num_kv_heads, head_dim / x, block_size, x],  x = 16 / elem_bytes
  *   v_cache : [num_blocks, num_kv_heads, head_dim, block_size]

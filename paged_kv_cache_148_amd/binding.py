@@ -20,7 +20,8 @@ PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA, PKV_PATH_TILE_VALU = 0, 1, 2, 3
 # every symbol include/pkv.h declares
 EXPORTS = ("paged_kv_write", "paged_attention_decode", "copy_blocks", "pkv_attention_workspace_size",
            "pkv_attention_path", "pkv_status_string", "paged_kv_write_head_major",
-           "paged_attention_decode_head_major", "pkv_attention_path_head_major", "pkv_stream_read_probe")
+           "paged_attention_decode_head_major", "pkv_attention_path_head_major", "pkv_stream_read_probe",
+           "paged_attention_decode_write")
 
 _lib = None
 
@@ -64,6 +65,9 @@ def lib():
         L.copy_blocks.argtypes = [p, p, p, i64, i32, i32, i32, i32, ctypes.c_int, p]
         L.pkv_status_string.restype = ctypes.c_char_p
         L.pkv_status_string.argtypes = [ctypes.c_int]
+        L.paged_attention_decode_write.restype = ctypes.c_int
+        L.paged_attention_decode_write.argtypes = [p, p, p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i32, i32,
+                                                   ctypes.c_float, i32, p, sz, ctypes.c_int, p]
         L.pkv_stream_read_probe.restype = ctypes.c_int
         L.pkv_stream_read_probe.argtypes = [p, sz, p, p]
         _lib = L
@@ -171,6 +175,33 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q, stream))
     _check(st, "paged_attention_decode")
+
+
+def paged_attention_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                 max_context_len: int, scale: float, partition_size: int = 0, workspace=None,
+                                 stream=None) -> None:
+    """paged_kv_write of k_new[s], v_new[s] at position context_lens[s] - 1 of each sequence
+    (the slot from its table), then paged_attention_decode; one launch on the tile paths."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, B, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q/out [S, Hq, D] and caches [N, B, Hkv, D]")
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+        raise ValueError("k_new and v_new must be [S, Hkv, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    if workspace is None:
+        need = attention_workspace_size(S, Hq, D, max_context_len, partition_size)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    dt = q.dtype
+    st = lib().paged_attention_decode_write(
+        _dev(out, "out", dt), _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B,
+        N, float(scale), int(partition_size), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(q, stream))
+    _check(st, "paged_attention_decode_write")
 
 
 # ---------------------------------------------------------------------------

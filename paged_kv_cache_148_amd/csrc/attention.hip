@@ -82,6 +82,8 @@ struct AttnArgs {
   unsigned *queue;   // [0]: items taken beyond the grid (zero between calls)
   int persistent;    // 1: persistent workgroups + work queue; 0: one workgroup per possible item
   float cls_scale;   // length classes of the longest-first schedule: kClasses / (min(P, max_ctx) + 1)
+  const void *k_new; // [S, Hkv, D]: each sequence's new K row, stored at position ctx - 1 by the
+  const void *v_new; //   item that attends to it (the fused write; null otherwise)
 };
 
 // Work-item order across the chip.  Workgroups go round-robin to the 8 XCDs by their
@@ -764,9 +766,11 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
 // heads, a real contraction).  !MF: one query head per KV head -- the tiles' K and V row pieces
 // meet q and P in fp32 FMAs on exactly widened elements, and q.k is summed over a 16-lane row
 // by DPP (an MFMA would leave 15 of its 16 columns empty).
-template <int B, int NB, bool HM, bool MF>
+// FUSE: the fused write of each sequence's new token (row layout only; see load_item_new).
+template <int B, int NB, bool HM, bool MF, bool FUSE = false>
 __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
+  static_assert(!FUSE || !HM, "the fused write is built for the row layout");
   static_assert(NB >= 2, "the ring holds the tile being computed and at least one ahead");
   constexpr int D = 128;
   __shared__ TileSmem sm;
@@ -828,6 +832,46 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     load_item_q(cur, qop);
     int bad_cur = 0, bad_next = 0;
 
+    // The fused write.  The item whose partition holds a sequence's new token (position
+    // ctx - 1) stores that token's K and V rows of its KV head, from k_new and v_new, into the
+    // token's slot, and the wave whose tile holds the token puts the same bytes in place of the
+    // (stale) row it loaded before using it: the row is used from registers, so nothing waits
+    // on the store.  Lane (c16, grp) holds bytes 16 c16 .. 16 c16 + 15 of its rows, so each lane
+    // loads that piece of the new rows, with the item's q.
+    u32x4 kn_cur = {0u, 0u, 0u, 0u}, vn_cur = kn_cur, kn_nxt = kn_cur, vn_nxt = kn_cur;
+    // the item's partition holds the context's last token
+    auto is_last = [&](const MItem &it) -> bool {
+      const int c = a.persistent ? sm_ctx[it.s] : a.ctx[it.s];
+      return it.fill == 0 && it.t1 == __builtin_amdgcn_readfirstlane(c);
+    };
+    auto load_item_new = [&](const MItem &it, u32x4 &kn, u32x4 &vn) {
+      if constexpr (FUSE) {
+        const uint32_t range = is_last(it) ? (uint32_t)(D * 2) : 0u;
+        const size_t row = ((size_t)it.s * a.Hkv + it.kvh) * D;
+        kn = __builtin_amdgcn_raw_buffer_load_b128(
+            buf_rsrc(reinterpret_cast<const uint16_t *>(a.k_new) + row, range), 16 * c16, 0, 0);
+        vn = __builtin_amdgcn_raw_buffer_load_b128(
+            buf_rsrc(reinterpret_cast<const uint16_t *>(a.v_new) + row, range), 16 * c16, 0, 0);
+      }
+    };
+    // this wave's index of the tile holding the item's new token, or -1
+    auto new_tile = [&](const MItem &it) -> int {
+      if (!FUSE || !is_last(it)) return -1;
+      const int rel = ((it.t1 - 1) >> 4) - it.tile_lo;
+      return rel % kWaves == wave ? rel / kWaves : -1;
+    };
+    // the table entry of the new token's block is taken when its tile is issued (-1: outside
+    // the pool, so the row is not stored); hn: that block among the tile's
+#define PKV_NEW_BLOCK(IT, RAW, DST)                                             \
+  do {                                                                          \
+    const int hn_ = BPT == 1 ? 0 : (((IT).t1 - 1) & 15) / B;                    \
+    int e_ = (RAW)[0];                                                          \
+    _Pragma("unroll") for (int h_ = 1; h_ < BPT; ++h_) if (h_ == hn_) e_ = (RAW)[h_]; \
+    (DST) = (unsigned)e_ < (unsigned)a.N ? e_ : -1;                             \
+  } while (0)
+    load_item_new(cur, kn_cur, vn_cur);
+    int new_i_cur = new_tile(cur), new_i_nxt = -1, new_phys_cur = -1, new_phys_nxt = -1;
+
     // Loads of tile i of an item (zero-range descriptors past its live tiles).
     auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const bool live = i < it.n_my;
@@ -877,9 +921,14 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
       }
       const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
       int phys[BPT];
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
+        if (i == new_i_cur) PKV_NEW_BLOCK(cur, phys, new_phys_cur);
+      }
 #pragma unroll
       for (int h = 0; h < BPT; ++h) {
-        phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
+        if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
         if ((unsigned)phys[h] >= (unsigned)a.N) {
           if (live && tok0 + h * B < cur.t1) bad_cur = 1;   // an entry the range reads
           phys[h] = 0;
@@ -891,9 +940,14 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const int tok0 = (nxt.tile_lo + wave + kWaves * i) << 4;
       int phys[BPT];
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
+        if (i == new_i_nxt) PKV_NEW_BLOCK(nxt, phys, new_phys_nxt);
+      }
 #pragma unroll
       for (int h = 0; h < BPT; ++h) {
-        phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
+        if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
         if ((unsigned)phys[h] >= (unsigned)a.N) {
           if (i < nxt.n_my && tok0 + h * B < nxt.t1) bad_next = 1;
           phys[h] = 0;
@@ -912,6 +966,25 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
 
     auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
       const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      if constexpr (FUSE) {
+        if (i == new_i_cur) {
+          // the new token's place in the tile, and the load (lane group, instruction) of it
+          const int t = (cur.t1 - 1) & 15;
+          const int gn = BPT == 1 ? t >> 2 : (t % B) / RPI;
+          const int rn = BPT == 1 ? (t & 3) : (t / B) * RPI + (t % B) % RPI;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool mine = grp == gn && r == rn;
+            kr[r] = mine ? kn_cur : kr[r];
+            vr[r] = mine ? vn_cur : vr[r];
+          }
+          if (new_phys_cur >= 0 && grp == 0) {
+            const size_t off = ((size_t)new_phys_cur * B + (cur.t1 - 1) % B) * tsb + (size_t)cur.kvh * D * 2;
+            __builtin_amdgcn_raw_buffer_store_b128(kn_cur, buf_rsrc(kpool + off, D * 2), 16 * c16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(vn_cur, buf_rsrc(vpool + off, D * 2), 16 * c16, 0, 0);
+          }
+        }
+      }
       if constexpr (!MF && HM) {
         // head-major, one query head: lane (c16, grp) holds K chunks 4c + grp of tile row c16
         // and the V pieces of rows 4grp .. 4grp + 3 at dims 16j + c16
@@ -1095,6 +1168,9 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
       table_chunks<B>(a, nxt, 0, wave, lane, tb_next);
       table_chunks<B>(a, nxt, 1, wave, lane, tb_next_ahead);
       load_item_q(nxt, qnext);
+      load_item_new(nxt, kn_nxt, vn_nxt);
+      new_i_nxt = new_tile(nxt);
+      new_phys_nxt = -1;
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
       // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
       // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
@@ -1192,6 +1268,10 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
       w = wn;
       wn = a.persistent ? sm.nextw[k & 1] : total;
       cur = nxt;
+      kn_cur = kn_nxt;
+      vn_cur = vn_nxt;
+      new_i_cur = new_i_nxt;
+      new_phys_cur = new_phys_nxt;
 #pragma unroll
       for (int h = 0; h < BPT; ++h) {
         tb_cur[h] = tb_next[h];
@@ -1574,6 +1654,12 @@ static pkv_path select_path_head_major(int Hq, int Hkv, int D, int B, pkv_dtype 
 
 typedef void (*Pass1Fn)(AttnArgs);
 
+// kv_copy.hip: the new tokens' rows to the slots of positions ctx - 1, from the tables
+pkv_status launch_kv_write_last(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                const int32_t *tables, int max_blocks, const int32_t *ctx, int max_ctx, int num_seqs,
+                                int num_blocks, int block_size, int num_kv_heads, int head_dim, int elem_bytes,
+                                void *stream);
+
 template <typename T, int D, int G>
 static Pass1Fn vec_fn_b(int B) {
   switch (B) {
@@ -1594,15 +1680,15 @@ static Pass1Fn vec_fn(int g, int B) {
   }
 }
 
-template <bool MF, int NB>
+template <bool MF, int NB, bool FUSE = false>
 static Pass1Fn tile_fn(int B) {
   switch (B) {
-    case 4: return attn_tile_kernel<4, NB, false, MF>;
-    case 8: return attn_tile_kernel<8, NB, false, MF>;
-    case 16: return attn_tile_kernel<16, NB, false, MF>;
-    case 32: return attn_tile_kernel<32, NB, false, MF>;
-    case 64: return attn_tile_kernel<64, NB, false, MF>;
-    default: return attn_tile_kernel<128, NB, false, MF>;
+    case 4: return attn_tile_kernel<4, NB, false, MF, FUSE>;
+    case 8: return attn_tile_kernel<8, NB, false, MF, FUSE>;
+    case 16: return attn_tile_kernel<16, NB, false, MF, FUSE>;
+    case 32: return attn_tile_kernel<32, NB, false, MF, FUSE>;
+    case 64: return attn_tile_kernel<64, NB, false, MF, FUSE>;
+    default: return attn_tile_kernel<128, NB, false, MF, FUSE>;
   }
 }
 
@@ -1618,7 +1704,13 @@ static Pass1Fn tile_hm_fn(int B) {
 
 // deep: the MFMA tiles' deep load ring (split into partitions of at most 512 tokens).  One
 // query head per KV head keeps the shallow ring: its merge and stores are a single head's.
-static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major, bool deep) {
+// fuse: the fused write of the new tokens (row layout, tile paths, shallow ring: the new rows
+// take the registers the deep ring would need).
+static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major, bool deep, bool fuse) {
+  if (fuse) {
+    return path == PKV_PATH_MFMA ? tile_fn<true, kTileDepthShallow, true>(B)
+                                 : tile_fn<false, kTileDepthShallow, true>(B);
+  }
   if (head_major) {
     if (path == PKV_PATH_TILE_VALU) return tile_hm_fn<false, kTileDepthShallow>(B);
     return deep ? tile_hm_fn<true, kTileDepthDeep>(B) : tile_hm_fn<true, kTileDepthShallow>(B);
@@ -1680,7 +1772,9 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
                          const int32_t *block_tables, int32_t max_blocks_per_seq, const int32_t *context_lens,
                          int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
-                         void *workspace, size_t workspace_bytes, pkv_dtype dtype, void *stream) {
+                         void *workspace, size_t workspace_bytes, pkv_dtype dtype, void *stream,
+                         const void *k_new = nullptr, const void *v_new = nullptr) {
+  const bool fuse = k_new != nullptr || v_new != nullptr;
   if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
       max_blocks_per_seq < 1 || max_context_len < 1 || partition_size < 0)
@@ -1689,6 +1783,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   const pkv_path path = head_major ? select_path_head_major(num_heads, num_kv_heads, head_dim, block_size, dtype)
                                    : select_path(num_heads, num_kv_heads, head_dim, block_size, dtype);
   if (path == PKV_PATH_NONE) return PKV_ERR_UNSUPPORTED;
+  if (fuse && head_major) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PKV_ERR_INVALID_ARG;
   if (partition_size > 0 && partition_size % block_size != 0) return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
@@ -1700,6 +1795,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
       !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return PKV_ERR_INVALID_ARG;
   if (!(scale == scale)) return PKV_ERR_INVALID_ARG;
+  if (fuse && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return PKV_ERR_INVALID_ARG;
 
   const int64_t P = partition_size > 0 ? partition_size : ((int64_t)max_context_len + 15) / 16 * 16;
   const int64_t np = parts_for(max_context_len, P);
@@ -1729,12 +1825,28 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   a.scale_log2 = scale * kLog2e;
   a.S = num_seqs;
   a.cls_scale = (float)kClasses / (float)((P < max_context_len ? P : max_context_len) + 1);
+  a.k_new = k_new;
+  a.v_new = v_new;
 
   hipStream_t st = (hipStream_t)stream;
   const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty
   if (items > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   const bool bf16 = dtype == PKV_DTYPE_BF16;
-  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, np > 1 && P <= kDeepRingMaxPartition);
+  // The write rides in the attention launch on the tile paths, except where the MFMA tiles
+  // want the deep ring (short partitions: the new rows would take its registers) -- there, and
+  // on the vector path, the same write is a launch of its own just before the attention.
+  const bool deep = path == PKV_PATH_MFMA && np > 1 && P <= kDeepRingMaxPartition;
+  const bool fuse_in_tiles = fuse && !deep && (path == PKV_PATH_MFMA || path == PKV_PATH_TILE_VALU);
+  if (fuse && !fuse_in_tiles) {
+    // (the caches are written only when the caller passed them writable: the fused entry point)
+    const pkv_status ws = launch_kv_write_last(k_new, v_new, const_cast<void *>(k_cache), const_cast<void *>(v_cache),
+                                               block_tables, max_blocks_per_seq,
+                                               context_lens, max_context_len, num_seqs, num_blocks, block_size,
+                                               num_kv_heads, head_dim, bf16 ? 2 : 4, stream);
+    if (ws != PKV_OK) return ws;
+    a.k_new = a.v_new = nullptr;
+  }
+  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, deep, fuse_in_tiles);
   // persistent workgroups when the schedule fits in LDS, else one workgroup per possible item
   size_t dyn_lds = 0;
   int64_t grid = items;
@@ -1777,6 +1889,20 @@ extern "C" pkv_status paged_attention_decode(void *out, const void *q, const voi
   return decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, workspace,
                 workspace_bytes, dtype, stream);
+}
+
+extern "C" pkv_status paged_attention_decode_write(void *out, const void *q, const void *k_new, const void *v_new,
+                                                   void *k_cache, void *v_cache, const int32_t *block_tables,
+                                                   int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                                   int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                   int32_t num_blocks, float scale, int32_t partition_size,
+                                                   void *workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                                   void *stream) {
+  if (!k_new || !v_new) return PKV_ERR_INVALID_ARG;
+  return decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, workspace,
+                workspace_bytes, dtype, stream, k_new, v_new);
 }
 
 extern "C" pkv_status paged_attention_decode_head_major(

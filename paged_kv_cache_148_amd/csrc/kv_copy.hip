@@ -113,6 +113,45 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(u32x4 *__rest
   }
 }
 
+// The new token of each decode step: k_new[s], v_new[s] to the slot of position ctx[s] - 1,
+// the slot taken from the sequence's table (the write paged_attention_decode_write makes when
+// its attention runs as a launch of its own).  Nothing is written for a context outside
+// [1, max_ctx] or a table entry outside the pool.
+__global__ __launch_bounds__(kWriteThreads) void kv_write_last_kernel(
+    const u32x4 *__restrict__ k_new, const u32x4 *__restrict__ v_new, u32x4 *__restrict__ k_cache,
+    u32x4 *__restrict__ v_cache, const int32_t *__restrict__ tables, int max_blocks, const int32_t *__restrict__ ctx,
+    int max_ctx, int num_blocks, int block_size, int row_vecs) {
+  const int s = blockIdx.x;
+  const int c = ctx[s];
+  if (c < 1 || c > max_ctx) return;
+  const int blk = tables[(int64_t)s * max_blocks + (c - 1) / block_size];
+  if (blk < 0 || blk >= num_blocks) return;
+  const int64_t slot = (int64_t)blk * block_size + (c - 1) % block_size;
+  const int c0 = (int)blockIdx.y * kWriteChunk + (int)threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < kWriteVecs; ++i) {
+    const int v = c0 + i * kWriteThreads;
+    if (v < row_vecs) {
+      k_cache[slot * row_vecs + v] = k_new[(int64_t)s * row_vecs + v];
+      v_cache[slot * row_vecs + v] = v_new[(int64_t)s * row_vecs + v];
+    }
+  }
+}
+
+// Launches kv_write_last_kernel (host checks are the caller's).
+pkv_status launch_kv_write_last(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                const int32_t *tables, int max_blocks, const int32_t *ctx, int max_ctx, int num_seqs,
+                                int num_blocks, int block_size, int num_kv_heads, int head_dim, int elem_bytes,
+                                void *stream) {
+  const int64_t row_vecs = (int64_t)num_kv_heads * head_dim * elem_bytes / 16;
+  const int64_t chunks = (row_vecs + kWriteChunk - 1) / kWriteChunk;
+  if (chunks > 65535 || num_seqs > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(kv_write_last_kernel, dim3((unsigned)num_seqs, (unsigned)chunks), dim3(kWriteThreads), 0,
+                     (hipStream_t)stream, (const u32x4 *)k_new, (const u32x4 *)v_new, (u32x4 *)k_cache,
+                     (u32x4 *)v_cache, tables, max_blocks, ctx, max_ctx, num_blocks, block_size, (int)row_vecs);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 static bool shape_ok(int32_t block_size, int32_t num_kv_heads, int32_t head_dim) {
   return (head_dim == 64 || head_dim == 128) &&
          (block_size == 4 || block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64 ||

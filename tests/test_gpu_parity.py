@@ -795,3 +795,93 @@ def test_stream_read_probe_runs():
     torch.cuda.synchronize()
     assert torch.equal(buf, before)
 
+
+# ---------------------------------------------------------------------------
+# the write fused into the attention launch
+# ---------------------------------------------------------------------------
+
+FUSED = [
+    # workload or shape, sequences, step, partition sizes
+    ("mha7b", 6, "steady", (0, 512)),
+    ("gqa70b", 12, "steady", (0, 256, 2048)),
+    ("fork_cow", None, "fork", (512, 0)),
+    ("long_splitk", None, "steady", (512,)),
+    (("bf16", 4, 8, 8, 128, 4, (1, 300)), None, "steady", (0, 64)),      # g = 1, B = 4
+    (("bf16", 4, 6, 2, 128, 8, (1, 200)), None, "steady", (0, 48)),      # g = 3, B = 8
+    (("bf16", 4, 24, 8, 128, 32, (1, 400)), None, "steady", (0, 128)),   # g = 3, B = 32
+    (("bf16", 3, 16, 2, 128, 128, (1, 2600)), None, "steady", (0, 512)), # g = 8, B = 128
+    ("tiny_fp32", None, "steady", (0, 8)),                                # the vector path
+    (("bf16", 4, 16, 2, 64, 8, (1, 200)), None, "steady", (0, 64)),      # vector, D = 64, g = 8
+]
+
+
+def _fused_wl(spec, num_seqs):
+    if isinstance(spec, str):
+        if spec == "long_splitk":
+            return _wl(spec, ctx=np.array([5000, 12345, 1, 700], np.int64))
+        return _wl(spec, num_seqs=num_seqs)
+    dt, S, Hq, Hkv, D, B, (lo, hi) = spec
+    return workloads.make_workload(workloads.Config("fused", dt, S, Hq, Hkv, D, B, ("uniform", lo, hi), seed=7 + Hq + B))
+
+
+@pytest.mark.parametrize("spec,num_seqs,which,parts", FUSED, ids=[str(f[0]) if isinstance(f[0], str) else
+                                                              f"g{f[0][2] // f[0][3]}-B{f[0][5]}" for f in FUSED])
+def test_fused_write_equals_write_then_attend(spec, num_seqs, which, parts):
+    # paged_attention_decode_write gives the caches and the output of paged_kv_write followed by
+    # paged_attention_decode, bit for bit (the slot comes from the table, the new rows from
+    # k_new / v_new), and those are the oracle's: in one launch on the tile paths, as a launch of
+    # its own before the attention for short MFMA partitions and on the vector path
+    import torch
+    wl = _fused_wl(spec, num_seqs)
+    step = pbatch.step_for(wl, which)
+    for P in parts:
+        _say("fused write", wl.cfg.name, which, "P", P)
+        d1 = H.upload(wl, step)
+        H.gpu_step(wl, step, d1, P)
+        d2 = H.upload(wl, step)
+        if step.copy_pairs.shape[0]:
+            binding.copy_blocks(d2["k_cache"], d2["v_cache"], d2["copy_pairs"])
+        binding.paged_attention_decode_write(d2["out"], d2["q"], d2["k_new"], d2["v_new"], d2["k_cache"],
+                                             d2["v_cache"], d2["block_tables"], d2["context_lens"],
+                                             step.max_context_len, wl.scale, P)
+        torch.cuda.synchronize()
+        assert H.bits(d2["k_cache"]).tobytes() == H.bits(d1["k_cache"]).tobytes()
+        assert H.bits(d2["v_cache"]).tobytes() == H.bits(d1["v_cache"]).tobytes()
+        assert H.bits(d2["out"]).tobytes() == H.bits(d1["out"]).tobytes()
+    _, kc, _, ref = H.oracle_step(wl, which, parts[0])
+    assert H.bits(d2["k_cache"]).tobytes() == kc.tobytes()
+
+
+def test_fused_write_bad_values_write_nothing():
+    # a sequence with context 0, one with a context above the host bound and one whose new
+    # token's table entry lies outside the pool: their outputs as paged_attention_decode gives
+    # them, and no byte of either pool changes for them; the others are written and attended
+    import torch
+    wl = _wl("gqa70b", num_seqs=6)
+    step = pbatch.step_for(wl)
+    B = wl.cfg.block_size
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, 0, do_attn=False)
+    written_k = H.bits(d["k_cache"]).copy()
+    e = H.upload(wl, step)
+    before_k = H.bits(e["k_cache"]).copy()
+    ctx = e["context_lens"].clone()
+    bt = e["block_tables"].clone()
+    ctx[0] = 0
+    ctx[2] = step.max_context_len + 5
+    c3 = int(step.context_lens[3])
+    bt[3, (c3 - 1) // B] = wl.num_blocks + 1000
+    binding.paged_attention_decode_write(e["out"], e["q"], e["k_new"], e["v_new"], e["k_cache"], e["v_cache"], bt, ctx,
+                                         step.max_context_len, wl.scale, 0)
+    torch.cuda.synchronize()
+    o = H.widen(H.bits(e["out"]))
+    assert (o[0] == 0).all() and np.isnan(o[2]).all() and np.isnan(o[3]).all()
+    got_k = H.bits(e["k_cache"])
+    slots = step.slot_mapping.tolist()
+    for s_, sl in enumerate(slots):
+        want = before_k if s_ in (0, 2, 3) else written_k
+        assert got_k[sl // B, sl % B].tobytes() == want[sl // B, sl % B].tobytes(), f"sequence {s_}"
+    H.gpu_step(wl, step, d, 0, do_copy=False, do_write=False)
+    for s_ in (1, 4, 5):
+        assert H.bits(e["out"])[s_].tobytes() == H.bits(d["out"])[s_].tobytes()
+
