@@ -733,13 +733,18 @@ def test_large_batch_uses_fallback_grid():
 # the decode step replayed from a HIP graph
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,num_seqs,P,which", [("mha7b", 8, 0, "steady"), ("gqa70b", 16, 512, "steady"),
-                                                   ("fork_cow", None, 512, "fork"), ("tiny_fp32", None, 8, "steady")])
-def test_decode_step_replays_from_a_hip_graph(name, num_seqs, P, which):
-    # copy_blocks -> paged_kv_write -> paged_attention_decode captured once and replayed: the calls
-    # allocate and clear nothing, and each attention call leaves its queue counters at zero, so
-    # every replay -- with eager calls on the same workspace and torch's own kernels in between --
-    # gives the eager step's caches and output bit for bit
+@pytest.mark.parametrize("name,num_seqs,P,which,fused", [("mha7b", 8, 0, "steady", False),
+                                                         ("gqa70b", 16, 512, "steady", False),
+                                                         ("fork_cow", None, 512, "fork", False),
+                                                         ("tiny_fp32", None, 8, "steady", False),
+                                                         ("mha7b", 8, 0, "steady", True),
+                                                         ("fork_cow", None, 1024, "fork", True)])
+def test_decode_step_replays_from_a_hip_graph(name, num_seqs, P, which, fused):
+    # copy_blocks -> paged_kv_write -> paged_attention_decode (or copy_blocks ->
+    # paged_attention_decode_write) captured once and replayed: the calls allocate and clear
+    # nothing, and each attention call leaves its queue counters at zero, so every replay -- with
+    # eager calls on the same workspace and torch's own kernels in between -- gives the eager
+    # step's caches and output bit for bit
     import torch
     wl = _wl(name, num_seqs=num_seqs)
     cfg = wl.cfg
@@ -750,6 +755,11 @@ def test_decode_step_replays_from_a_hip_graph(name, num_seqs, P, which):
     def run(d, out):
         if step.copy_pairs.shape[0]:
             binding.copy_blocks(d["k_cache"], d["v_cache"], d["copy_pairs"])
+        if fused:
+            binding.paged_attention_decode_write(out, d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"],
+                                                 d["block_tables"], d["context_lens"], step.max_context_len,
+                                                 wl.scale, P, ws)
+            return
         binding.paged_kv_write(d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["slot_mapping"])
         binding.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
                                        d["context_lens"], step.max_context_len, wl.scale, P, ws)
