@@ -42,6 +42,7 @@
 
 #include "pkv.h"
 #include "pkv_device.h"
+#include "pkv_internal.h"
 
 namespace pkv {
 
@@ -945,6 +946,7 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
         for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
         if (i == new_i_nxt) PKV_NEW_BLOCK(nxt, phys, new_phys_nxt);
       }
+#undef PKV_NEW_BLOCK
 #pragma unroll
       for (int h = 0; h < BPT; ++h) {
         if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
@@ -1653,12 +1655,6 @@ static pkv_path select_path_head_major(int Hq, int Hkv, int D, int B, pkv_dtype 
 }
 
 typedef void (*Pass1Fn)(AttnArgs);
-
-// kv_copy.hip: the new tokens' rows to the slots of positions ctx - 1, from the tables
-pkv_status launch_kv_write_last(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                                const int32_t *tables, int max_blocks, const int32_t *ctx, int max_ctx, int num_seqs,
-                                int num_blocks, int block_size, int num_kv_heads, int head_dim, int elem_bytes,
-                                void *stream);
 
 template <typename T, int D, int G>
 static Pass1Fn vec_fn_b(int B) {

@@ -9,6 +9,7 @@
 
 #include "pkv.h"
 #include "pkv_device.h"
+#include "pkv_internal.h"
 
 namespace pkv {
 
@@ -138,7 +139,6 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_last_kernel(
   }
 }
 
-// Launches kv_write_last_kernel (host checks are the caller's).
 pkv_status launch_kv_write_last(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                                 const int32_t *tables, int max_blocks, const int32_t *ctx, int max_ctx, int num_seqs,
                                 int num_blocks, int block_size, int num_kv_heads, int head_dim, int elem_bytes,
