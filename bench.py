@@ -286,7 +286,8 @@ def movers(steps: int = 20) -> dict:
     blocks of 16 slots, 8 KV heads, head_dim 128, bf16 (32 KiB per block per tensor): a write of
     131072 tokens to distinct slots scattered over the pool (256 MiB of K and V each way), and a
     copy of 8192 (src, dst) block pairs (also 256 MiB each way).  One pair of HIP events around
-    `steps` back-to-back calls on the launch stream."""
+    `steps` back-to-back calls on the launch stream.  Beside them, torch's contiguous device copy
+    of the same bytes, as the rate a copy without indirection reaches."""
     import torch
     from paged_kv_cache_148_amd import binding
     N, B, Hkv, D = 16384, 16, 8, 128
@@ -321,6 +322,18 @@ def movers(steps: int = 20) -> dict:
                      "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] {name}: {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s", file=sys.stderr, flush=True)
     del kc, vc, kn, vn, slots, pairs
+    # Context: the runtime's own contiguous device copy of the same 512 MiB each way (no slot or
+    # pair indirection): what a plain copy reaches on this machine.
+    src = torch.empty(2 * T * row, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src))
+    nbytes = 2 * src.numel()
+    res["contiguous_device_copy"] = {"us": round(t * 1e6, 2), "algorithmic_bytes": nbytes,
+                                     "GB/s": round(nbytes / t / 1e9, 1),
+                                     "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+    print(f"[bench] contiguous device copy (torch copy_): {t * 1e6:.1f} us, {nbytes / t / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
+    del src, dst
     torch.cuda.empty_cache()
     return {"results": res, "tokens_written": T, "pairs_copied": N // 2, "steps": steps,
             "timing": f"HIP events around {steps} back-to-back calls on the launch stream"}

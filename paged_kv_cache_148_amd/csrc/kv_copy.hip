@@ -13,6 +13,25 @@
 
 namespace pkv {
 
+// Calls that write at least this many bytes load and store with the non-temporal hint: their
+// destination is larger than what the next launch could find in cache, and with the hint on both
+// sides the bulk write ran 2-3% faster (level with the runtime's own contiguous device copy).
+// Smaller calls -- every decode step's write and copy-on-write copies -- keep the cached forms,
+// since the attention launch right after them reads what they wrote (with the hint the fused fork
+// step took 0.8 us longer).
+constexpr int64_t kStreamingMoveBytes = int64_t(32) << 20;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 mv_load(const u32x4 *p) {
+  if constexpr (NT) return ld16_stream(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void mv_store(u32x4 *p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // One workgroup per (token, 4 KiB chunk of its row), grid-stride over tokens beyond the
 // grid.  A slot names one [Hkv, D] row of the pool; consecutive slots are consecutive rows,
 // so the row of slot s = b * B + o starts s * row_vecs 16-byte vectors into the pool.  The
@@ -21,6 +40,7 @@ namespace pkv {
 constexpr int kWriteThreads = 128;
 constexpr int kWriteVecs = 2;                               // 16-byte vectors per thread and tensor
 constexpr int kWriteChunk = kWriteThreads * kWriteVecs;     // vectors of a row per workgroup
+template <bool NT>
 __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(const u32x4 *__restrict__ k_new,
                                                                  const u32x4 *__restrict__ v_new,
                                                                  u32x4 *__restrict__ k_cache,
@@ -37,8 +57,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(const u32x4 *__
     for (int i = 0; i < kWriteVecs; ++i) {
       const int c = c0 + i * kWriteThreads;
       if (c < row_vecs) {
-        kv[i] = ks[c];
-        vv[i] = vs[c];
+        kv[i] = mv_load<NT>(ks + c);
+        vv[i] = mv_load<NT>(vs + c);
       }
     }
     if (slot < 0 || slot >= num_slots) continue;  // -1 / out of range: no write
@@ -48,8 +68,8 @@ __global__ __launch_bounds__(kWriteThreads) void kv_write_kernel(const u32x4 *__
     for (int i = 0; i < kWriteVecs; ++i) {
       const int c = c0 + i * kWriteThreads;
       if (c < row_vecs) {
-        kd[c] = kv[i];
-        vd[c] = vv[i];
+        mv_store<NT>(kd + c, kv[i]);
+        mv_store<NT>(vd + c, vv[i]);
       }
     }
   }
@@ -90,6 +110,7 @@ constexpr int kCopyVecsPerThread = 4;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyChunk = kCopyThreads * kCopyVecsPerThread;
 
+template <bool NT>
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(u32x4 *__restrict__ k_cache,
                                                                    u32x4 *__restrict__ v_cache,
                                                                    const int64_t *__restrict__ pairs,
@@ -105,12 +126,12 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(u32x4 *__rest
 #pragma unroll
   for (int i = 0; i < kCopyVecsPerThread; ++i) {
     const int64_t c = c0 + (int64_t)i * kCopyThreads;
-    if (c < block_vecs) buf[i] = s[c];
+    if (c < block_vecs) buf[i] = mv_load<NT>(s + c);
   }
 #pragma unroll
   for (int i = 0; i < kCopyVecsPerThread; ++i) {
     const int64_t c = c0 + (int64_t)i * kCopyThreads;
-    if (c < block_vecs) d[c] = buf[i];
+    if (c < block_vecs) mv_store<NT>(d + c, buf[i]);
   }
 }
 
@@ -184,9 +205,11 @@ extern "C" pkv_status paged_kv_write(const void *k_new, const void *v_new, void 
   if (chunks > 65535) return PKV_ERR_UNSUPPORTED;
   const int row_vecs = (int)row_vecs64;
   const unsigned grid = (unsigned)(num_tokens < (1 << 20) ? num_tokens : (1 << 20));
-  hipLaunchKernelGGL(kv_write_kernel, dim3(grid, (unsigned)chunks), dim3(kWriteThreads), 0, (hipStream_t)stream,
-                     (const u32x4 *)k_new, (const u32x4 *)v_new, (u32x4 *)k_cache, (u32x4 *)v_cache, slot_mapping,
-                     num_tokens, row_vecs, (int64_t)num_blocks * block_size);
+  const bool nt = 2 * num_tokens * row_vecs64 * 16 >= kStreamingMoveBytes;
+  hipLaunchKernelGGL(nt ? kv_write_kernel<true> : kv_write_kernel<false>, dim3(grid, (unsigned)chunks),
+                     dim3(kWriteThreads), 0, (hipStream_t)stream, (const u32x4 *)k_new, (const u32x4 *)v_new,
+                     (u32x4 *)k_cache, (u32x4 *)v_cache, slot_mapping, num_tokens, row_vecs,
+                     (int64_t)num_blocks * block_size);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -232,8 +255,10 @@ extern "C" pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *b
   const int64_t block_vecs = (int64_t)block_size * num_kv_heads * head_dim * elem / 16;
   const int64_t chunks = (block_vecs + kCopyChunk - 1) / kCopyChunk;
   if (chunks > 65535) return PKV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)chunks, 2), dim3(kCopyThreads), 0,
-                     (hipStream_t)stream, (u32x4 *)k_cache, (u32x4 *)v_cache, block_mapping, block_vecs, num_blocks);
+  const bool nt = 2 * num_pairs * block_vecs * 16 >= kStreamingMoveBytes;
+  hipLaunchKernelGGL(nt ? copy_blocks_kernel<true> : copy_blocks_kernel<false>,
+                     dim3((unsigned)num_pairs, (unsigned)chunks, 2), dim3(kCopyThreads), 0, (hipStream_t)stream,
+                     (u32x4 *)k_cache, (u32x4 *)v_cache, block_mapping, block_vecs, num_blocks);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

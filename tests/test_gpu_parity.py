@@ -145,6 +145,48 @@ def test_write_and_copy_large_blocks_bit_exact(B):
     assert H.bits(d["v_cache"]).tobytes() == vc.tobytes()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_bulk_write_and_copy_bit_exact(dt):
+    # calls that move 32 MiB or more take the non-temporal forms of both kernels; one call
+    # each a little above that size and one just below, over a pool of arbitrary bit patterns
+    import torch
+    rng = np.random.default_rng(31)
+    N, B, Hkv, D = 2048, 16, 8, 128
+    udt, sdt = (np.uint16, np.int16) if dt == "bf16" else (np.uint32, np.int32)
+    fdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    host = (lambda a: a) if dt == "bf16" else (lambda a: a.view(np.float32))   # the oracle's dtypes
+
+    def bits(shape):
+        return rng.integers(0, np.iinfo(udt).max, size=shape, dtype=udt, endpoint=True)
+
+    def dev(a):
+        return torch.from_numpy(a.view(sdt)).cuda().view(fdt)
+
+    kc, vc = bits((N, B, Hkv, D)), bits((N, B, Hkv, D))
+    dk, dv = dev(kc), dev(vc)
+    row = Hkv * D * kc.itemsize
+    tk = (32 << 20) // (2 * row)                       # tokens whose K and V rows make 32 MiB
+    for T in (tk + 7, tk - 1):
+        kn, vn = bits((T, Hkv, D)), bits((T, Hkv, D))
+        slots = rng.permutation(N * B)[:T].astype(np.int64)
+        _say("bulk write", dt, T)
+        binding.paged_kv_write(dev(kn), dev(vn), dk, dv, torch.from_numpy(slots).cuda())
+        torch.cuda.synchronize()
+        oracle.kv_write(host(kn), host(vn), host(kc), host(vc), slots)
+        assert H.bits(dk).tobytes() == kc.tobytes()
+        assert H.bits(dv).tobytes() == vc.tobytes()
+    pk = (32 << 20) // (2 * B * row)                   # pairs whose K and V blocks make 32 MiB
+    for P in (pk + 3, pk - 1):
+        perm = rng.permutation(N)
+        pairs = np.stack([perm[:P], perm[P:2 * P]], axis=1).astype(np.int64)
+        _say("bulk copy", dt, P)
+        binding.copy_blocks(dk, dv, torch.from_numpy(pairs).cuda())
+        torch.cuda.synchronize()
+        oracle.copy_blocks(host(kc), host(vc), pairs)
+        assert H.bits(dk).tobytes() == kc.tobytes()
+        assert H.bits(dv).tobytes() == vc.tobytes()
+
+
 # ---------------------------------------------------------------------------
 # attention on the configurations (sizes the oracle finishes in seconds)
 # ---------------------------------------------------------------------------
