@@ -29,6 +29,7 @@ def _pack(m, seqs, ctx, slots, pairs):
         "context_lens": ctx,
         "slot_mapping": np.asarray(slots, dtype=np.int64),
         "copy_pairs": np.asarray(pairs, dtype=np.int64).reshape(-1, 2),
+        "holders": np.asarray(m.holder_counts(), dtype=np.int32),   # per block id, after the step
     }
 
 

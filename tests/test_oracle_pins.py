@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle.blocks import BlockModel, build_tables
+from oracle import batch as obatch
+from oracle.blocks import BlockModel, PrefixModel, build_tables
 from tests.conftest import golden
 import workloads
 
@@ -174,6 +175,135 @@ def test_block_model_random_ops_invariants():
             s = live.pop(int(rng.integers(len(live))))
             m.release(s["table"])
         m.check(live)
+
+
+# ---------------------------------------------------------------------------
+# prefix reuse model: the pages' ten-copies case, and scenarios worked by hand
+# ---------------------------------------------------------------------------
+
+def _prompt(n, salt=0):
+    return [(7 * i + salt) % 50021 for i in range(n)]
+
+
+@pytest.mark.parametrize("case", golden("prefix_sharing.json")["cases"], ids=lambda c: f"{c['prompt_tokens']}")
+def test_prefix_model_ten_requests_share_one_prompt(case):
+    B = golden("prefix_sharing.json")["block_size"]
+    L, R = case["prompt_tokens"], case["requests"]
+    plain = BlockModel(2000, B)
+    copies = [plain.new_sequence(L) for _ in range(R)]
+    assert len(plain.ref) == case["blocks_without_sharing"]          # ten copies
+    plain.check(copies)
+    m = BlockModel(2000, B)
+    pm = PrefixModel(m)
+    res = [pm.new_sequence(_prompt(L)) for _ in range(R)]
+    assert [h for _, h in res] == case["reused_blocks_per_request"]
+    assert len(m.ref) == case["blocks_with_sharing"]
+    shared = res[0][0]["table"][:case["full_blocks"]]
+    assert all(r["table"][:case["full_blocks"]] == shared for r, _ in res)
+    assert all(m.ref[b] == case["shared_refcount"] for b in shared)
+    private = [b for r, _ in res for b in r["table"][case["full_blocks"]:]]
+    assert len(private) == len(set(private)) == R * case["private_blocks_per_request"]
+    m.check([r for r, _ in res])
+
+
+def test_prefix_model_divergent_shifted_and_released():
+    # B = 4, worked by hand: a block is reused only when every token up to its end matches
+    m = BlockModel(64, 4)
+    pm = PrefixModel(m)
+    a, ha = pm.new_sequence([1, 2, 3, 4, 5, 6, 7, 8, 9])               # 2 full blocks + 1 slot
+    b, hb = pm.new_sequence([1, 2, 3, 4, 5, 6, 7, 8, 10, 11, 12, 13])  # both full blocks reused
+    c, hc = pm.new_sequence([1, 2, 3, 4, 5, 6, 0, 8])                  # diverges inside block 1
+    d, hd = pm.new_sequence([9, 9, 9, 9, 5, 6, 7, 8])                  # a's block 1 ids, other prefix
+    assert (ha, hb, hc, hd) == (0, 2, 1, 0)
+    assert b["table"][:2] == a["table"][:2] and b["table"][2] != a["table"][2]
+    assert c["table"][0] == a["table"][0] and c["table"][1] not in a["table"]
+    assert not set(d["table"]) & set(a["table"] + b["table"] + c["table"])
+    assert len(a["table"]) == 3 and a["table"][2] not in b["table"]     # a's partial block is private
+    assert m.ref[a["table"][0]] == 3 and m.ref[a["table"][1]] == 2
+    assert len(m.ref) == 3 + 1 + 1 + 2                                 # a: 3, b: +1, c: +1, d: +2
+    m.check([a, b, c, d])
+    for s in (a, b, c):
+        pm.release(s)
+    e, he = pm.new_sequence([1, 2, 3, 4, 5, 6, 7, 8])                  # every holder gone: no hit
+    assert he == 0 and len(pm.by_prefix) == 4                           # d's two blocks and e's two
+    f, hf = pm.new_sequence([9, 9, 9, 9, 5, 6, 7, 8, 1])                # d's prefix is still held
+    assert hf == 2 and f["table"][:2] == d["table"]
+    m.check([d, e, f])
+
+
+def test_prefix_model_same_block_ids_under_two_prefixes():
+    # block 1 of [X, C] and of [Y, C] hold the same token ids but different KV (they attend to
+    # different prefixes): a third prompt [X, C] must reuse the first prompt's blocks
+    X, Y, C = [1, 1, 1, 1], [2, 2, 2, 2], [3, 3, 3, 3]
+    m = BlockModel(32, 4)
+    pm = PrefixModel(m)
+    p1, _ = pm.new_sequence(X + C)
+    p2, h2 = pm.new_sequence(Y + C)
+    p3, h3 = pm.new_sequence(X + C)
+    assert h2 == 0 and h3 == 2
+    assert p3["table"] == p1["table"] and not set(p2["table"]) & set(p1["table"])
+    m.check([p1, p2, p3])
+
+
+def test_prefix_model_out_of_blocks_changes_nothing():
+    m = BlockModel(6, 4)
+    pm = PrefixModel(m)
+    a, _ = pm.new_sequence(list(range(16)))                             # 4 blocks
+    before = (m.free, m.ref, dict(pm.by_prefix))
+    assert pm.new_sequence(list(range(8)) + [99] * 12) is None          # 2 hits + 3 new > 2 free
+    assert (m.free, m.ref, dict(pm.by_prefix)) == before
+    m.check([a])
+
+
+# ---------------------------------------------------------------------------
+# the fork workload's step inputs: counts the workload's statement fixes
+# (16 sequences on one 2000-token prompt, refcount 16; at 16-token blocks 2000 = 125 x 16,
+# so the shared prompt is 125 full blocks).  Reading: the parent also holds its first
+# generated token (position 2000, alone in block 125), so that block is the partly filled
+# shared one whose copy-on-write the step needs; children write before the parent.
+# ---------------------------------------------------------------------------
+
+def _fork_setup(seed=5, extra=40):
+    cfg = workloads.CONFIGS["fork_cow"]
+    rng = np.random.default_rng(seed)
+    gen = rng.integers(80, 512, size=cfg.num_seqs, endpoint=True)
+    need = 126 + sum(-(-int(2001 + g) // 16) - 125 for g in gen) + extra
+    return cfg, gen, need, [int(x) for x in rng.permutation(need)]
+
+
+def test_oracle_fork_step_counts():
+    cfg, _, N, order = _fork_setup()
+    B, S = cfg.block_size, cfg.num_seqs
+    o = obatch.fork_step(2000, S - 1, N, B, order)
+    tb, pairs, ctx, slots = o["block_tables"], o["copy_pairs"], o["context_lens"], o["slot_mapping"]
+    assert (ctx == 2002).all() and tb.shape == (S, 126)
+    assert pairs.shape == (S - 1, 2)                                  # one copy per child
+    parent_last = int(tb[0, 125])
+    assert (pairs[:, 0] == parent_last).all()                         # all from the shared last block
+    assert len(set(pairs[:, 1].tolist())) == S - 1 and parent_last not in pairs[:, 1]
+    assert sorted(tb[1:, 125].tolist()) == sorted(pairs[:, 1].tolist())
+    assert (tb[:, :125] == tb[0, :125]).all()                         # 125 prompt blocks shared
+    assert slots.tolist() == [int(tb[s, 125]) * B + 1 for s in range(S)]   # position 2001
+    h = o["holders"]
+    assert (h[tb[0, :125]] == S).all() and int((h == S).sum()) == 125
+    assert h[parent_last] == 1 and (h[pairs[:, 1]] == 1).all()
+    assert int(h.sum()) == 125 * S + S
+
+
+def test_oracle_steady_fork_step_counts():
+    cfg, gen, N, order = _fork_setup()
+    B, S = cfg.block_size, cfg.num_seqs
+    o = obatch.steady_fork_step(2000, gen, N, B, order)
+    tb, pairs, ctx, slots = o["block_tables"], o["copy_pairs"], o["context_lens"], o["slot_mapping"]
+    assert ctx.tolist() == [2001 + int(g) for g in gen]
+    assert pairs.shape == (0, 2)                                      # no copy left in the step
+    assert (tb[:, :125] == tb[0, :125]).all()
+    h = o["holders"]
+    assert int((h == S).sum()) == 125 and (h[tb[0, :125]] == S).all()
+    private = [int(b) for s in range(S) for b in tb[s, 125:-(-int(ctx[s]) // B)]]
+    assert len(private) == len(set(private)) and all(h[b] == 1 for b in private)
+    assert len(private) == sum(-(-int(c) // B) - 125 for c in ctx)
+    assert slots.tolist() == [int(tb[s, (int(ctx[s]) - 1) // B]) * B + (int(ctx[s]) - 1) % B for s in range(S)]
 
 
 # ---------------------------------------------------------------------------
