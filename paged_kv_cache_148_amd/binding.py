@@ -1,7 +1,8 @@
 """Thin Python binding over libpkv.so's C ABI (include/pkv.h).
 
-Argument marshalling only: tensors become device pointers and sizes, the stream
-is torch's current HIP stream, and a non-OK status raises PkvError.  Every step
+Argument marshalling only: tensors become device pointers and sizes, the launch
+stream is the call's `stream` argument (a torch.cuda.Stream or a raw handle) or
+else torch's current HIP stream, and a non-OK status raises PkvError.  Every step
 of the computation runs in the library's HIP kernels; there is no fallback path,
 so a missing or unloadable library raises immediately.
 """
@@ -108,9 +109,32 @@ def _dev(t, name: str, dtype=None):
 
 
 def _stream(t, stream):
-    if stream is not None:
-        return ctypes.c_void_p(int(stream))
-    return ctypes.c_void_p(_torch().cuda.current_stream(t.device).cuda_stream)
+    """Raw hipStream_t of the launch stream: `stream` (a torch.cuda.Stream or a raw handle), else
+    torch's current stream on t's device."""
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _workspace(workspace, nbytes: int, t, stream):
+    """The caller's workspace, or a fresh one whose work-queue header is zeroed on the launch
+    stream itself (so the zero-fill precedes the launch) and which the caching allocator does not
+    hand out again before the work queued on that stream is done."""
+    if workspace is not None:
+        return workspace
+    torch = _torch()
+    if stream is None:
+        # the launch stream is torch's current stream: memory freed when this call returns is only
+        # reused by work queued after the launch on that same stream
+        return torch.zeros(nbytes, dtype=torch.uint8, device=t.device)
+    st = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=t.device)
+    with torch.cuda.stream(st):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=t.device)
+    ws.record_stream(st)
+    return ws
 
 
 def attention_workspace_size(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
@@ -154,7 +178,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over each sequence's table.
 
     workspace: a device buffer of at least attention_workspace_size(...) bytes whose first
-    256 bytes were zeroed when it was allocated (a fresh zeroed one is made if None)."""
+    256 bytes were zeroed when it was allocated (if None, a fresh one is zeroed on the launch
+    stream).  stream: a torch.cuda.Stream or a raw hipStream_t handle; None = torch's current
+    stream."""
     torch = _torch()
     S, Hq, D = q.shape
     N, B, Hkv, D2 = k_cache.shape
@@ -162,10 +188,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("shape mismatch between q/out [S, Hq, D] and caches [N, B, Hkv, D]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    if workspace is None:
-        # zeroed: its leading work-queue counters must start at zero
-        need = attention_workspace_size(S, Hq, D, max_context_len, partition_size)
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    # zeroed when made here: its leading work-queue counters must start at zero
+    workspace = _workspace(workspace, attention_workspace_size(S, Hq, D, max_context_len, partition_size), q, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr())
     ws_bytes = workspace.numel() * workspace.element_size()
     dt = q.dtype
@@ -191,9 +215,7 @@ def paged_attention_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_t
         raise ValueError("k_new and v_new must be [S, Hkv, D]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    if workspace is None:
-        need = attention_workspace_size(S, Hq, D, max_context_len, partition_size)
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, attention_workspace_size(S, Hq, D, max_context_len, partition_size), q, stream)
     dt = q.dtype
     st = lib().paged_attention_decode_write(
         _dev(out, "out", dt), _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
@@ -260,9 +282,7 @@ def paged_attention_decode_head_major(out, q, k_cache, v_cache, block_tables, co
         raise ValueError("shape mismatch between q/out [S, Hq, D] and the caches")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
         raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
-    if workspace is None:
-        need = attention_workspace_size(S, Hq, D, max_context_len, partition_size)
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, attention_workspace_size(S, Hq, D, max_context_len, partition_size), q, stream)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr())
     ws_bytes = workspace.numel() * workspace.element_size()
     dt = q.dtype

@@ -696,6 +696,31 @@ def test_two_streams_with_their_own_workspaces():
         assert not ws[:8].any().item()
 
 
+@pytest.mark.parametrize("as_handle", [False, True], ids=["torch-stream", "raw-handle"])
+def test_explicit_stream_without_workspace(as_handle):
+    # a side stream passed as `stream=` with no workspace: the binding zeroes a fresh workspace on
+    # that stream and keeps it until the launch is done; torch's current stream stays idle
+    import torch
+    wl = _wl("gqa70b", num_seqs=12)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, 0, do_attn=False)
+    side = torch.cuda.Stream()
+    st = side.cuda_stream if as_handle else side
+    outs = []
+    _say("explicit stream", "handle" if as_handle else "torch stream")
+    for P in (512, 0, 512):
+        o = torch.full_like(d["out"], float("nan"))
+        side.wait_stream(torch.cuda.current_stream())
+        binding.paged_attention_decode(o, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                       step.max_context_len, wl.scale, P, stream=st)
+        outs.append((P, o))
+    side.synchronize()
+    for P, o in outs:
+        _, _, _, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(H.bits(o), ref, "bf16", f"explicit stream P={P}")
+
+
 @pytest.mark.parametrize("name,num_seqs,which,P", [("fork_cow", None, "fork", 512), ("mha7b", 6, "steady", 0)])
 def test_pool_beyond_4_gib(name, num_seqs, which, P):
     # every block the step touches lies past the first 4 GiB of a pool of more than 4 GiB per
