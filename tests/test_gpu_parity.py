@@ -499,25 +499,21 @@ def test_head_major_unread_slots_and_padding_never_read(heads):
         assert H.bits(d["out"]).tobytes() == clean.tobytes()
 
 
-@pytest.mark.parametrize("name", ["gqa70b", "mha7b"])
-def test_head_major_full_size_sampled_parity(name):
+@pytest.mark.parametrize("name", ["gqa70b", "mha7b", "long_splitk"])
+def test_head_major_full_size_parity(name):
+    # every output element of the full-size configuration on head-major caches
     wl = _wl(name)
     step = pbatch.step_for(wl)
-    cfg = wl.cfg
-    rng = np.random.default_rng(13)
-    items = np.unique(rng.integers(0, cfg.num_seqs * cfg.num_heads, size=96))
-    for P in ((0, 2048) if name == "gqa70b" else (0,)):
-        _say("head-major sampled", name, "P", P)
+    for P in ((0, 2048) if name == "gqa70b" else (BENCH_PARTITION[name],)):
+        _say("head-major full", name, "P", P)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P, do_attn=False)
         khm, vhm = pbatch.to_head_major(d["k_cache"], d["v_cache"])
         binding.paged_attention_decode_head_major(d["out"], d["q"], khm, vhm, d["block_tables"],
                                                   d["context_lens"], step.max_context_len, wl.scale, P)
-        o, kc, vc, _ = H.oracle_step(wl, "steady", P, attend=False)
-        ref = oracle.attention(wl.q, kc, vc, o["block_tables"], o["context_lens"], wl.scale, P, items)
-        got = H.bits(d["out"]).reshape(cfg.num_seqs * cfg.num_heads, -1)[items]
-        H.check_close(got, ref, "bf16", f"head-major {name} P={P}")
-        del khm, vhm
+        o, kc, vc, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(H.bits(d["out"]), ref, "bf16", f"head-major full {name} P={P}")
+        del khm, vhm, d
 
 
 @pytest.mark.parametrize("heads", [(4, 4), (8, 2)], ids=["g1", "g4"])
@@ -549,14 +545,16 @@ def test_split_matches_unsplit_within_tolerance():
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations, in the bench's launch configuration, on sampled outputs
+# full-size configurations, in the bench's launch configuration, every output element
 # ---------------------------------------------------------------------------
 
 from bench import PARTITION as BENCH_PARTITION  # noqa: E402  (the partitions bench.py times)
 
 
-@pytest.mark.parametrize("name", ["mha7b", "gqa70b", "long_splitk", "fork_cow"])
-def test_full_size_sampled_parity(name):
+@pytest.mark.parametrize("name", ["tiny_fp32", "mha7b", "gqa70b", "long_splitk", "fork_cow"])
+def test_full_size_parity(name):
+    # the whole [S, Hq, D] output of each configuration at its full size against the fp64 oracle,
+    # and both pools after the step's copies and writes bit for bit
     wl = _wl(name)
     P = BENCH_PARTITION[name]
     whiches = ["fork", "steady"] if name == "fork_cow" else ["steady"]
@@ -565,21 +563,13 @@ def test_full_size_sampled_parity(name):
         _say("full", name, which, "S", wl.cfg.num_seqs, "P", P, "pool", wl.k_cache.shape)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P)
-        S, Hq = wl.cfg.num_seqs, wl.cfg.num_heads
-        rng = np.random.default_rng(11)
-        items = np.unique(np.concatenate([rng.integers(0, S * Hq, size=48), [0, S * Hq - 1]]))
-        # longest and shortest sequences always included
-        for s in (int(np.argmax(step.context_lens)), int(np.argmin(step.context_lens))):
-            items = np.unique(np.concatenate([items, [s * Hq, s * Hq + Hq - 1]]))
-        o, kc, vc, ref = H.oracle_step(wl, which, P, items=items)
-        got = H.bits(d["out"]).reshape(S * Hq, -1)[items]
-        H.check_close(got, ref, wl.cfg.dtype, f"full {name}/{which}")
-        # the written rows, bit-exact, on every sequence
-        B = wl.cfg.block_size
-        kg = H.bits(d["k_cache"])
-        for s, sl in enumerate(step.slot_mapping.tolist()):
-            assert kg[sl // B, sl % B].tobytes() == kc[sl // B, sl % B].tobytes()
-        del d
+        o, kc, vc, ref = H.oracle_step(wl, which, P)
+        assert np.array_equal(o["block_tables"], step.block_tables) and np.array_equal(o["copy_pairs"],
+                                                                                      step.copy_pairs)
+        H.check_close(H.bits(d["out"]), ref, wl.cfg.dtype, f"full {name}/{which} P={P}")
+        assert np.array_equal(H.bits(d["k_cache"]), kc), f"{name}/{which}: K pool"
+        assert np.array_equal(H.bits(d["v_cache"]), vc), f"{name}/{which}: V pool"
+        del d, kc, vc
 
 
 # ---------------------------------------------------------------------------
@@ -925,8 +915,10 @@ def test_fused_write_equals_write_then_attend(spec, num_seqs, which, parts):
         assert H.bits(d2["k_cache"]).tobytes() == H.bits(d1["k_cache"]).tobytes()
         assert H.bits(d2["v_cache"]).tobytes() == H.bits(d1["v_cache"]).tobytes()
         assert H.bits(d2["out"]).tobytes() == H.bits(d1["out"]).tobytes()
-    _, kc, _, ref = H.oracle_step(wl, which, parts[0])
-    assert H.bits(d2["k_cache"]).tobytes() == kc.tobytes()
+        _, kc, vc, ref = H.oracle_step(wl, which, P)
+        assert H.bits(d2["k_cache"]).tobytes() == kc.tobytes()
+        assert H.bits(d2["v_cache"]).tobytes() == vc.tobytes()
+        H.check_close(H.bits(d2["out"]), ref, wl.cfg.dtype, f"fused {wl.cfg.name}/{which} P={P}")
 
 
 def test_fused_write_bad_values_write_nothing():
