@@ -19,7 +19,9 @@
  * Ownership and threading: every array argument is a DEVICE pointer owned by the
  * caller.  The library allocates nothing, keeps no state between calls and never
  * synchronises: each call only enqueues kernels on `stream` (a hipStream_t; NULL
- * is the default stream) and returns.  Calls are thread-safe.
+ * is the default stream) and returns.  Calls are thread-safe.  The one exception is
+ * paged_attention_decode_noalloc, whose scratch is a static device array of the library
+ * (described with it).
  *
  * Errors: host-visible argument checks return a status before anything is
  * enqueued (the pages' allocator reports failure by return value rather than by
@@ -48,7 +50,8 @@ typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, workspace too small */
   PKV_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, block_size, group size, dtype */
-  PKV_ERR_HIP = 3            /* the HIP runtime rejected a launch */
+  PKV_ERR_HIP = 3,           /* the HIP runtime rejected a launch */
+  PKV_ERR_SCRATCH_LIMIT = 4  /* paged_attention_decode_noalloc: the call needs more than the static scratch */
 } pkv_status;
 
 typedef enum { PKV_DTYPE_F32 = 0, PKV_DTYPE_BF16 = 1 } pkv_dtype;
@@ -230,6 +233,32 @@ pkv_path pkv_attention_path_head_major(int32_t num_heads, int32_t num_kv_heads, 
  * `stream`, like every call here.
  */
 pkv_status pkv_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+/*
+ * paged_attention_decode_noalloc -- for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): paged_attention_decode
+ * with the same arguments but no workspace.  The work-queue header and the split's partial states
+ * live in a static device array of the library, pkv_static_scratch_bytes() = 64 MiB, which every
+ * device the library runs on holds from the first call until the process ends.  Nothing is
+ * allocated or freed by the call; results are those of paged_attention_decode (the same kernels).
+ *
+ * The first call on a device (the current device) looks up that device's array and clears its
+ * work-queue header with a small kernel on `stream`; every call leaves the header at zero again.
+ * All calls on one device share its array: calls that may overlap on one device (two streams,
+ * two threads, or a graph replay beside an eager call) race and must not be issued.  A call
+ * whose workspace need (pkv_attention_workspace_size) exceeds the array returns
+ * PKV_ERR_SCRATCH_LIMIT before anything is enqueued; other checks and device-value handling as
+ * for paged_attention_decode.
+ */
+pkv_status paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache, const void *v_cache,
+                                          const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t *context_lens, int32_t max_context_len, int32_t num_seqs,
+                                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t num_blocks, float scale,
+                                          int32_t partition_size, pkv_dtype dtype, void *stream);
+
+/* Bytes of the static scratch array behind paged_attention_decode_noalloc (per device). */
+size_t pkv_static_scratch_bytes(void);
 
 /* Static, human-readable name of a status code. */
 const char *pkv_status_string(pkv_status status);

@@ -14,7 +14,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpkv.so")
 
-PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP = 0, 1, 2, 3
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 PKV_DTYPE_F32, PKV_DTYPE_BF16 = 0, 1
 PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA, PKV_PATH_TILE_VALU = 0, 1, 2, 3
 
@@ -22,7 +22,7 @@ PKV_PATH_NONE, PKV_PATH_VECTOR, PKV_PATH_MFMA, PKV_PATH_TILE_VALU = 0, 1, 2, 3
 EXPORTS = ("paged_kv_write", "paged_attention_decode", "copy_blocks", "pkv_attention_workspace_size",
            "pkv_attention_path", "pkv_status_string", "paged_kv_write_head_major",
            "paged_attention_decode_head_major", "pkv_attention_path_head_major", "pkv_stream_read_probe",
-           "paged_attention_decode_write")
+           "paged_attention_decode_write", "paged_attention_decode_noalloc", "pkv_static_scratch_bytes")
 
 _lib = None
 
@@ -71,6 +71,11 @@ def lib():
                                                    ctypes.c_float, i32, p, sz, ctypes.c_int, p]
         L.pkv_stream_read_probe.restype = ctypes.c_int
         L.pkv_stream_read_probe.argtypes = [p, sz, p, p]
+        L.paged_attention_decode_noalloc.restype = ctypes.c_int
+        L.paged_attention_decode_noalloc.argtypes = [p, p, p, p, p, i32, p, i32, i32, i32, i32, i32, i32, i32,
+                                                     ctypes.c_float, i32, ctypes.c_int, p]
+        L.pkv_static_scratch_bytes.restype = sz
+        L.pkv_static_scratch_bytes.argtypes = []
         _lib = L
     return _lib
 
@@ -199,6 +204,31 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
         float(scale), int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(q, stream))
     _check(st, "paged_attention_decode")
+
+
+def static_scratch_bytes() -> int:
+    """Bytes of the library's static device scratch behind paged_attention_decode_noalloc."""
+    return int(lib().pkv_static_scratch_bytes())
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len: int,
+                                   scale: float, partition_size: int = 0, stream=None) -> None:
+    """paged_attention_decode with its scratch in the library's static device array: nothing is
+    allocated, here or in the library.  Calls that may overlap on one device must not be issued."""
+    torch = _torch()
+    S, Hq, D = q.shape
+    N, B, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(out.shape) != (S, Hq, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q/out [S, Hq, D] and caches [N, B, Hkv, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or tuple(context_lens.shape) != (S,):
+        raise ValueError("block_tables must be [S, max_blocks] and context_lens [S]")
+    dt = q.dtype
+    st = lib().paged_attention_decode_noalloc(
+        _dev(out, "out", dt), _dev(q, "q", dt), _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), int(max_context_len), S, Hq, Hkv, D, B, N,
+        float(scale), int(partition_size), _dtype_code(q), _stream(q, stream))
+    _check(st, "paged_attention_decode_noalloc")
 
 
 def paged_attention_decode_write(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,

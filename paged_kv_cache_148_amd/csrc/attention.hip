@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pkv.h"
 #include "pkv_device.h"
 #include "pkv_internal.h"
@@ -1914,4 +1916,71 @@ extern "C" pkv_status paged_attention_decode_head_major(
 extern "C" pkv_path pkv_attention_path_head_major(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                                   int32_t block_size, pkv_dtype dtype) {
   return select_path_head_major(num_heads, num_kv_heads, head_dim, block_size, dtype);
+}
+
+// ---------------------------------------------------------------------------
+// paged_attention_decode_noalloc: the same call with the workspace in a static device array
+// ---------------------------------------------------------------------------
+
+// The work-queue header and the split's partial states of paged_attention_decode_noalloc, laid
+// out as the caller's workspace is.  Every device the library runs on holds its own copy at its
+// own address for the life of the process.  Host code never passes this name to a kernel or a
+// copy (on the host it only stands for the symbol): it uses the address hipGetSymbolAddress
+// returns for the current device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace pkv {
+
+__global__ void clear_words_kernel(unsigned *p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mutex;
+static void *g_scratch[kMaxScratchDevices];
+
+// Device address of the current device's scratch.  The first call on a device looks it up and
+// clears its work-queue header with a small kernel on `st` (not a memset, so that a call under
+// graph capture records a kernel node); every attention call leaves the header at zero again.
+static pkv_status static_scratch(hipStream_t st, void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return PKV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_HIP;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<unsigned *>(p),
+                       (int)(kQueueBytes / sizeof(unsigned)));
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" size_t pkv_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" pkv_status paged_attention_decode_noalloc(void *out, const void *q, const void *k_cache,
+                                                     const void *v_cache, const int32_t *block_tables,
+                                                     int32_t max_blocks_per_seq, const int32_t *context_lens,
+                                                     int32_t max_context_len, int32_t num_seqs, int32_t num_heads,
+                                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                     int32_t num_blocks, float scale, int32_t partition_size,
+                                                     pkv_dtype dtype, void *stream) {
+  // the sizes decode() checks first; then the limit, before anything is looked up or enqueued
+  if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || max_context_len < 1 || partition_size < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size) >
+      kStaticScratchBytes)
+    return PKV_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  const pkv_status st = static_scratch((hipStream_t)stream, &ws);
+  if (st != PKV_OK) return st;
+  return decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, ws,
+                kStaticScratchBytes, dtype, stream);
 }

@@ -268,6 +268,7 @@ extern "C" const char *pkv_status_string(pkv_status status) {
     case PKV_ERR_INVALID_ARG: return "invalid argument";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PKV_ERR_HIP: return "HIP launch failure";
+    case PKV_ERR_SCRATCH_LIMIT: return "needs more scratch than the library's static scratch array holds";
   }
   return "unknown status";
 }

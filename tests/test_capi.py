@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_status_strings(L):
     assert binding.status_string(PKV_OK) == "ok"
-    for s in (1, 2, 3):
+    for s in (1, 2, 3, 4):
         assert binding.status_string(s) not in ("ok", "unknown status")
     assert binding.status_string(99) == "unknown status"
 
@@ -156,3 +156,17 @@ def test_stream_read_probe_rejects_bad_arguments(L):
     assert L.pkv_stream_read_probe(buf, 8, sink, None) == PKV_ERR_INVALID_ARG             # under one word
     assert L.pkv_stream_read_probe(ctypes.c_void_p(4100), 1 << 20, sink, None) == PKV_ERR_INVALID_ARG
     assert L.pkv_stream_read_probe(buf, 1 << 20, ctypes.c_void_p(258), None) == PKV_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_beyond_its_static_scratch_on_the_host(L):
+    # the limit is checked before anything is looked up or enqueued (no GPU needed): 64 sequences
+    # x 64 heads x 256 partitions of partial states are far beyond the 64 MiB array
+    assert L.pkv_static_scratch_bytes() == 64 << 20
+    assert binding.attention_workspace_size(64, 64, 128, 131072, 512) > L.pkv_static_scratch_bytes()
+    st = L.paged_attention_decode_noalloc(None, None, None, None, None, 8192, None, 131072, 64, 64, 8, 128, 16, 4,
+                                          0.1, 512, PKV_DTYPE_BF16, None)
+    assert st == binding.PKV_ERR_SCRATCH_LIMIT
+    assert "scratch" in binding.status_string(st)
+    st = L.paged_attention_decode_noalloc(None, None, None, None, None, 8192, None, 0, 64, 64, 8, 128, 16, 4,
+                                          0.1, 512, PKV_DTYPE_BF16, None)
+    assert st == PKV_ERR_INVALID_ARG                                     # max_context_len 0
