@@ -4,11 +4,13 @@ One step = copy_blocks (copy-on-write pairs, when the step has any) ->
 paged_kv_write (each sequence's newest token) -> paged_attention_decode, over one
 synthetic batch already resident in HBM.  Prints ONE JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload mha7b] [--only-main]
+    python bench.py [--steps K] [--warmup W] [--workload long_splitk] [--only-main]
 
-The headline workload is the 7B-shaped MHA decode layer; the GQA, long-context and
-fork/copy-on-write workloads are measured in the same run and reported under
-"workloads".  Byte counts are algorithmic: what the method must move (K and V of
+The line of record is the largest single-GPU workload, long-context split-K (8
+sequences of 32768..131072 tokens, 512-token partitions: 3.5 GB of K/V per step);
+the MHA, GQA, fork/copy-on-write and tiny fp32 workloads are measured in the same
+run and reported under "workloads", each with its own roofline and CPU oracle
+figure.  Byte counts are algorithmic: what the method must move (K and V of
 every attended position once per KV head, q, out, block-table entries, lengths, and
 the written / copied rows), not what the implementation happens to move.
 """
@@ -35,7 +37,7 @@ METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak), µs/decode ste
 HBM_PEAK_GBS = 8000.0
 # split-context partition used per workload (0 = one work unit per (sequence, KV head))
 PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": 1024}
-MAIN = "mha7b"
+MAIN = "long_splitk"
 
 
 def algorithmic_bytes(cfg, step) -> dict:
@@ -173,6 +175,15 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / steps
+    # the spread of the step: events around each whole step on the launch stream (each figure
+    # includes the events' own few microseconds)
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in sev:
+        a.record()
+        one_step()
+        b.record()
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in sev)
     # the same step captured once in a HIP graph and replayed (the calls allocate and clear
     # nothing, and the queue counters return to zero inside each attention call)
     graph = torch.cuda.CUDAGraph()
@@ -234,10 +245,14 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
         "us_per_step": step_s * 1e6, "us_per_step_graph": graph_step_s * 1e6,
+        "step_us_events": {"median": float(np.median(step_ms)) * 1e3, "p10": _pct(step_ms, 10) * 1e3,
+                           "p90": _pct(step_ms, 90) * 1e3,
+                           "timing": f"HIP events around each of {steps} whole steps (their own few us included)"},
         "us_per_step_fused": fused_step_s * 1e6 if fused_step_s else None, "attention_us_mean": attn_s * 1e6,
         "attention_us_events_mean": float(np.mean(attn_ms)) * 1e3, "mall_flushed_per_launch": flush_mall,
-        "attention_us_events_p10": attn_ms[len(attn_ms) // 10] * 1e3,
-        "attention_us_events_p90": attn_ms[(9 * len(attn_ms)) // 10] * 1e3,
+        "attention_us_events_median": float(np.median(attn_ms)) * 1e3,
+        "attention_us_events_p10": _pct(attn_ms, 10) * 1e3,
+        "attention_us_events_p90": _pct(attn_ms, 90) * 1e3,
         "step_gbs": nb["step"] / step_s / 1e9,
         "kv_gbs_attention": nb["kv"] / attn_s / 1e9,
         "attention_alg_gbs": nb["attention"] / attn_s / 1e9,
@@ -259,6 +274,52 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     del q, kc, vc, kn, vn, out, ws
     torch.cuda.empty_cache()
     return res, wl, step
+
+
+def _pct(sorted_vals, q: int) -> float:
+    """q-th percentile of an ascending list (nearest rank)."""
+    return float(sorted_vals[min(len(sorted_vals) - 1, max(0, -(-q * len(sorted_vals) // 100) - 1))])
+
+
+KERNEL_NAMES = {1: "paged_attention_decode (attn_vec_kernel)",
+                2: "paged_attention_decode (attn_tile_kernel, MFMA tiles)",
+                3: "paged_attention_decode (attn_tile_kernel, VALU dots: one query head per KV head)"}
+
+
+def roofline(name: str, res: dict, rd: dict | None) -> dict | None:
+    """The attention call against MI355X's 8 TB/s HBM peak: algorithmic bytes per call over the
+    mean duration of back-to-back calls on the launch stream.  None where the data the call reads
+    fits the 256 MB Infinity Cache (fork workload) or the call is latency-bound (tiny fp32)."""
+    if name in ("fork_cow", "tiny_fp32"):
+        return None
+    nb = res["bytes"]["attention"]
+    return {
+        "bound": "hbm",
+        "kernel": KERNEL_NAMES.get(res["path"], "paged_attention_decode"),
+        "achieved": round(res["attention_alg_gbs"], 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(res["attention_alg_gbs"] / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(name, nb),
+        "algorithmic_bytes_per_launch": nb,
+        "launch_us_mean": round(res["attention_us_mean"], 2),
+        "timing": f"HIP events around back-to-back attention calls on the launch stream",
+        "frac_of_stream_read": round(res["attention_alg_gbs"] / rd["GB/s"], 4) if rd else None,
+    }
+
+
+def read_probe(reps: int = 3, gib: int = 1) -> None:
+    """The plain streaming read over exactly `gib` GiB, `reps` times: the read-only reference for
+    scaling rocprofv3's FETCH_SIZE (a K/V stream is read-only)."""
+    import torch
+    from paged_kv_cache_148_amd import binding
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        binding.stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    print(json.dumps({"read_probe": True, "calls": reps, "bytes_read_per_call": gib << 30}), flush=True)
 
 
 def copy_probe(reps: int = 3) -> None:
@@ -365,32 +426,40 @@ def stream_read_ceiling(steps: int = 20, gib: int = 2) -> dict:
             "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0):
-    """The CPU oracle on the same inputs: whole-step passes (copies, write, attention) on all
-    host cores, repeated until about budget_s seconds have been spent."""
+def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0, threads: int = 0, max_reps: int = 200) -> dict:
+    """The CPU oracle on the same inputs: whole decode steps (copies, write, attention) on the
+    host, `threads` OpenMP threads (0: all it may use), repeated until about budget_s seconds have
+    been spent (at least once, at most max_reps times)."""
     import oracle
     cfg = wl.cfg
     nb = algorithmic_bytes(cfg, step)
+    nt = threads if threads > 0 else oracle.max_threads()
     reps, t_total = 0, 0.0
-    while reps == 0 or t_total < budget_s:
+    while reps == 0 or (t_total < budget_s and reps < max_reps):
         kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
         t = time.perf_counter()
         oracle.copy_blocks(kc, vc, step.copy_pairs)
         oracle.kv_write(wl.k_new, wl.v_new, kc, vc, step.slot_mapping)
-        oracle.attention(wl.q, kc, vc, step.block_tables, step.context_lens, wl.scale, partition)
+        oracle.attention(wl.q, kc, vc, step.block_tables, step.context_lens, wl.scale, partition, num_threads=nt)
         t_total += time.perf_counter() - t
         reps += 1
-        if reps >= 200:
-            break
+        del kc, vc
     per = t_total / reps
-    return {"value": nb["step"] / per / 1e9, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "us_per_step": per * 1e6,
+    return {"value": round(nb["step"] / per / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "us_per_step": round(per * 1e6, 1), "steps_timed": reps, "seconds": round(t_total, 2),
             "sample": f"{reps} whole decode step(s) of the {cfg.name} workload ({cfg.num_seqs} seqs, "
-                      f"{int(step.context_lens.sum())} tokens), fp64 scalar C + OpenMP, {t_total:.1f} s total",
-            "cpu": platform.processor() or _cpu_model()}
+                      f"{int(step.context_lens.sum())} tokens, partition {partition}), fp64 scalar C, "
+                      f"{nt} OpenMP thread(s), {t_total:.1f} s in all"}
 
 
-def _cpu_model():
+def host_info() -> dict:
+    """The host the CPU oracle runs on."""
+    import oracle
+    return {"cpu": _cpu_model(), "nproc": os.cpu_count(), "cpus_allowed": len(os.sched_getaffinity(0)),
+            "omp_threads": oracle.max_threads(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
@@ -398,7 +467,7 @@ def _cpu_model():
                     return ln.split(":", 1)[1].strip()
     except OSError:
         pass
-    return "unknown"
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -414,6 +483,8 @@ def main():
                     help="only time paged_kv_write and copy_blocks at HBM-bound sizes (256 MiB each way)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the plain streaming read over 1 GiB (counter calibration for rocprofv3)")
     ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous", "head_major"],
                     help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool; "
                          "head_major: the shuffled pool in the head-major cache layout")
@@ -434,6 +505,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.read_probe:
+        read_probe()
         return
     if args.movers:
         print(json.dumps({"movers": movers(), "kernel_source_hash": kernel_source_hash()}), flush=True)
@@ -459,27 +533,50 @@ def main():
         return
     res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
                             args.flush_mall)
-    print(f"[bench] {args.workload}: {res['us_per_step']:.1f} us/step ({res['us_per_step_graph']:.1f} from a graph, {res['us_per_step_fused'] or 0:.1f} fused), attention {res['attention_us_mean']:.1f} us, "
-          f"{res['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
-    cpu = None if args.no_cpu else cpu_baseline(wl, step, main_part)
-    del wl
+    _say_step(args.workload, res)
+    # the CPU oracle on each workload's own inputs, right after its GPU run (all host threads; the
+    # line of record's for ~10 s, the others once each; one thread as well on the two smallest)
+    cpu_runs = {}
+    if not args.no_cpu:
+        cpu_runs[args.workload] = cpu_baseline(wl, step, main_part, budget_s=10.0)
+        _say_cpu(args.workload, cpu_runs[args.workload])
+    del wl, step
     others = {}
+    single = {}
     if not args.only_main:
-        for name in ("gqa70b", "long_splitk", "fork_cow", "tiny_fp32"):
+        for name in OTHERS:
             if name == args.workload:
                 continue
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
-                r, _, _ = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
-                others[f"{name}/{w}" if name == "fork_cow" else name] = r
-                print(f"[bench] {name}/{w}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph, {r['us_per_step_fused'] or 0:.1f} fused), attention {r['attention_us_mean']:.1f} us,"
-                      f" {r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+                key = f"{name}/{w}" if name == "fork_cow" else name
+                r, wl_o, step_o = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
+                others[key] = r
+                _say_step(key, r)
+                if not args.no_cpu:
+                    cpu_runs[key] = cpu_baseline(wl_o, step_o, PARTITION[name], budget_s=0.0)
+                    _say_cpu(key, cpu_runs[key])
+                    if name in SINGLE_THREAD:
+                        single[key] = cpu_baseline(wl_o, step_o, PARTITION[name], budget_s=0.0, threads=1)
+                        _say_cpu(key + " (1 thread)", single[key])
+                del wl_o, step_o
 
     # paged_kv_write and copy_blocks where HBM, not launch latency, bounds them; a plain read
     mv = None if args.only_main else movers()
     rd = None if args.only_main else stream_read_ceiling()
     cfg = workloads.CONFIGS[args.workload]
-    nb = res["bytes"]
-    traffic = measured_traffic(args.workload, nb["attention"])
+    cpu = None
+    if cpu_runs:
+        cpu = dict(cpu_runs[args.workload])
+        cpu["host"] = host_info()
+        cpu["per_workload"] = {k: {kk: v[kk] for kk in ("value", "unit", "us_per_step", "cores", "steps_timed")}
+                               for k, v in cpu_runs.items()}
+        cpu["single_thread"] = {k: {kk: v[kk] for kk in ("value", "unit", "us_per_step", "cores", "steps_timed")}
+                                for k, v in single.items()}
+    workloads_out = {}
+    for k, v in others.items():
+        e = {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+        e["roofline"] = roofline(k.split("/")[0], v, rd)
+        workloads_out[k] = e
     line = {
         "metric": METRIC,
         "value": round(res["step_gbs"], 2),
@@ -496,38 +593,41 @@ def main():
         "config": {"workload": f"{args.workload}: {cfg.description}", "num_seqs": cfg.num_seqs,
                    "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
                    "block_size": res["block_size"], "partition_size": main_part, "sum_ctx": res["sum_ctx"],
-                   "parallelism": "single GPU"},
+                   "max_ctx": res["max_ctx"], "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
+        "step_us_events": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in res["step_us_events"].items()},
         "us_per_step_graph": round(res["us_per_step_graph"], 2),
         "us_per_step_fused": round(res["us_per_step_fused"], 2) if res["us_per_step_fused"] else None,
         "seqs_per_s": round(res["seqs_per_s"], 1),
         "host_step_us": round(res["host_step_us"], 1),
         "hbm_frac_step": round(res["step_gbs"] / HBM_PEAK_GBS, 4),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": {1: "paged_attention_decode (attn_vec_kernel)",
-                       2: "paged_attention_decode (attn_tile_kernel, MFMA tiles)",
-                       3: "paged_attention_decode (attn_tile_kernel, VALU dots: one query head per KV head)"}.get(
-                           res["path"], "paged_attention_decode"),
-            "achieved": round(res["attention_alg_gbs"], 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(res["attention_alg_gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": nb["attention"],
-            "launch_us_mean": round(res["attention_us_mean"], 2),
-            "timing": f"HIP events around {args.steps} back-to-back attention launches on the launch stream",
-            "launch_us_events_each": round(res["attention_us_events_mean"], 2),
-            "frac_of_stream_read": round(res["attention_alg_gbs"] / rd["GB/s"], 4) if rd else None,
-        },
+        "roofline": roofline(args.workload, res, rd),
+        "attention_us_events": {"median": round(res["attention_us_events_median"], 2),
+                                "p10": round(res["attention_us_events_p10"], 2),
+                                "p90": round(res["attention_us_events_p90"], 2)},
         "cpu_baseline": cpu,
-        "workloads": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                      for k, v in others.items()},
+        "workloads": workloads_out,
         "movers": mv,
         "stream_read": rd,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+# the other workloads of a default run, and those the CPU oracle also runs on one thread
+OTHERS = ("mha7b", "gqa70b", "long_splitk", "fork_cow", "tiny_fp32")
+SINGLE_THREAD = ("tiny_fp32", "mha7b")
+
+
+def _say_step(name, r):
+    print(f"[bench] {name}: {r['us_per_step']:.1f} us/step ({r['us_per_step_graph']:.1f} from a graph, "
+          f"{r['us_per_step_fused'] or 0:.1f} fused), attention {r['attention_us_mean']:.1f} us, "
+          f"{r['attention_alg_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+
+
+def _say_cpu(name, c):
+    print(f"[bench] CPU oracle {name}: {c['us_per_step']:.0f} us/step, {c['value']:.2f} GB/s, {c['cores']} thread(s), "
+          f"{c['steps_timed']} step(s)", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

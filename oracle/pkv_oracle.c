@@ -209,11 +209,12 @@ int oracle_paged_attention(double *out, const void *q, const void *k_cache, cons
   a.max_blocks = max_blocks; a.S = num_seqs; a.Hq = num_heads; a.Hkv = num_kv_heads;
   a.D = head_dim; a.B = block_size; a.N = num_blocks; a.scale = scale; a.dtype = dtype;
 #ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
+  /* a clause, not omp_set_num_threads: the count holds for this call only */
+  if (num_threads <= 0) num_threads = omp_get_max_threads();
 #else
   (void)num_threads;
 #endif
-#pragma omp parallel
+#pragma omp parallel num_threads(num_threads)
   {
     double *x = (double *)malloc(sizeof(double) * (size_t)max_ctx);
     double *o = (double *)malloc(sizeof(double) * (size_t)head_dim);

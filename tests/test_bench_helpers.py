@@ -42,3 +42,34 @@ def test_source_key_ignores_comments_and_layout():
     assert bench._code_only(code) == bench._code_only("/* a note */ int  f(int x)\n{ return x + 1; }")
     assert bench._code_only(code) != bench._code_only(code.replace("x + 1", "x + 2"))
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_percentiles_nearest_rank():
+    v = sorted(float(x) for x in range(1, 101))     # 1 .. 100
+    assert bench._pct(v, 10) == 10.0 and bench._pct(v, 90) == 90.0 and bench._pct(v, 100) == 100.0
+    assert bench._pct([5.0], 10) == 5.0
+
+
+def test_roofline_object():
+    res = {"bytes": {"attention": 3_500_000_000}, "attention_alg_gbs": 6000.0, "attention_us_mean": 583.3, "path": 2}
+    r = bench.roofline("long_splitk", res, {"GB/s": 6800.0})
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["frac"] == 0.75 and r["achieved"] == 6000.0 and r["algorithmic_bytes_per_launch"] == 3_500_000_000
+    assert abs(r["frac_of_stream_read"] - 6000 / 6800) < 1e-4
+    assert bench.roofline("fork_cow", res, None) is None       # Infinity-Cache resident: no HBM claim
+
+
+def test_host_info_names_the_cpu_model():
+    h = bench.host_info()
+    assert h["cpu"] not in ("", "x86_64", "unknown")            # the model name, not the ISA
+    assert h["nproc"] >= 1 and h["cpus_allowed"] >= 1 and h["omp_threads"] >= 1
+
+
+def test_cpu_baseline_on_the_tiny_workload():
+    import workloads
+    from paged_kv_cache_148_amd import batch
+    wl = workloads.make_workload("tiny_fp32")
+    step = batch.step_for(wl)
+    c = bench.cpu_baseline(wl, step, 0, budget_s=0.0, threads=1)
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["steps_timed"] == 1 and c["value"] > 0
+    assert "tiny_fp32" in c["sample"]
