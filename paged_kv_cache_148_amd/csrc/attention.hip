@@ -12,7 +12,8 @@
 // workgroup of 4 waves.  An item serves every query head of the KV head's group, so each
 // K/V byte is read once per group.  Without a partition size the partition is the whole
 // context.  With one, an item leaves a partial state (running max m, sum l, unnormalised
-// o) in the workspace and attn_reduce_kernel merges the partials by log-sum-exp;
+// o) as one contiguous record in the workspace and a second kernel merges the partials by
+// log-sum-exp;
 // sequences whose context fits one partition are finished in pass 1.
 //
 // Scheduling: the pass-1 kernels are persistent.  As many workgroups as fit on the chip
@@ -60,7 +61,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTileDepthShallow = 2;
 constexpr int kTileDepthDeep = 4;
 constexpr int64_t kDeepRingMaxPartition = 512;
-constexpr int kMaxReduceParts = 8192;    // partials per (seq, head) the reduce kernel stages in LDS (32 KiB)
+constexpr int kMaxReduceParts = 8192;    // partials per (sequence, head) a call may have
 constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
 constexpr int kClasses = 16;            // length classes of the longest-first schedule
 constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the workspace
@@ -72,9 +73,9 @@ struct AttnArgs {
   const void *v;
   const int32_t *tables;
   const int32_t *ctx;
-  float *ws_o;       // [S, Hq, max_parts, D]  unnormalised partial outputs
-  float *ws_ml;      // [S, Hkv, max_parts, 32]: (m, l) of query head j of the group at 2j, 2j+1;
-                     // m in the log2 domain.  One 128-byte line per item, written whole.
+  float *ws_rec;     // [S, Hkv, max_parts] records of g * D + 32 floats, one per item: the
+                     // group's unnormalised partial rows (head j at j * D), then a 128-byte line
+                     // of (m, l) pairs (head j at 2j, 2j + 1; m in the log2 domain), written whole
   int max_blocks;    // table row length
   int max_ctx;       // host bound on ctx
   int Hq, Hkv, g, N;
@@ -245,12 +246,11 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
     if (single) {
       store_out<T>(a.out, ((size_t)s * a.Hq + h) * D + d, o / L);
     } else {
-      const size_t part = ((size_t)s * a.Hq + h) * a.max_parts + p;
-      a.ws_o[part * D + d] = o;
+      float *rec = a.ws_rec + (((size_t)s * a.Hkv + kvh) * a.max_parts + p) * (size_t)(g * D + 32);
+      rec[j * D + d] = o;
       if (d == 0) {
-        float *ml = a.ws_ml + (((size_t)s * a.Hkv + kvh) * a.max_parts + p) * 32;
-        ml[2 * j] = M;
-        ml[2 * j + 1] = L;
+        rec[g * D + 2 * j] = M;
+        rec[g * D + 2 * j + 1] = L;
       }
     }
   }
@@ -735,24 +735,24 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
       __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((j * D + d0) * 2), 0, kStoreSc1);
     }
   } else {
+    // the item's record, one contiguous piece: the group's partial rows (head j at j * D), then
+    // its (m, l) line (zeros past the group).  Stored as one piece rather than g rows a
+    // partition-stride apart, the partials of a 512-token split cost the long contexts 5-7 us
+    // less (fewer DRAM pages written amid the K/V stream).
+    const size_t item = ((size_t)it.s * a.Hkv + it.kvh) * a.max_parts + it.p;
+    const uint32_t rec_bytes = (uint32_t)(a.g * D + 32) * 4;
+    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.ws_rec + item * (size_t)(a.g * D + 32), rec_bytes);
     if (act) {
-      // partial of head h0 + j at ((h0 + j) * max_parts + p) * D: g rows max_parts * D apart
-      const uint32_t row = (uint32_t)a.max_parts * D * 4;
-      const __amdgpu_buffer_rsrc_t ro =
-          buf_rsrc(a.ws_o + (h0 * a.max_parts + it.p) * D, (uint32_t)(a.g - 1) * row + D * 4);
-      const uint32_t off = (uint32_t)j * row + (uint32_t)d0 * 4;
+      const uint32_t off = (uint32_t)(j * D + d0) * 4;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), ro, off, 0, kStoreSc1);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), ro, off + 16, 0, kStoreSc1);
     }
-    // (m, l) of the group's heads fill the item's whole 128-byte line (zeros past the
-    // group): lanes 0, 32, .. write heads j and j + 1, so no line is shared between items
     const float M1 = __shfl_down(M, 16), L1 = __shfl_down(L, 16);   // head j + 1 is lane t + 16
     if ((t & 31) == 0) {
       const bool act1 = j + 1 < a.g;
       const f32x4 v = {act ? M : 0.f, act ? L : 0.f, act1 ? M1 : 0.f, act1 ? L1 : 0.f};
-      const size_t item = ((size_t)it.s * a.Hkv + it.kvh) * a.max_parts + it.p;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), buf_rsrc(a.ws_ml + item * 32, 128),
-                                             (uint32_t)(2 * j * 4), 0, kStoreSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, (uint32_t)(a.g * D + 2 * j) * 4, 0,
+                                             kStoreSc1);
     }
   }
 }
@@ -1515,76 +1515,82 @@ __global__ __launch_bounds__(kThreads) void attn_vec_kernel(const AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: merge the partials of one (sequence, head):
+// Pass 2: merge the partials of one (sequence, head), written in ascending partition order p:
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p l_p.
-// The partition -> thread assignment and the reduction trees are fixed, so the result
-// does not depend on timing.
+// The partition -> thread assignment and the merge order are fixed, so the result does not
+// depend on timing.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float *red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(v, off);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  __syncthreads();
-  return r;
+
+// Running log-sum-exp state (max m, sum l, accumulator) merged with the state (m2, l2, o2), in
+// that order: the pair's weights relative to the larger max (an empty state weighs 0).
+__device__ __forceinline__ void lse_merge(float &m, float &l, f32x4 &acc, float m2, float l2, const f32x4 &o2) {
+  const float mn = fmaxf(m, m2);
+  const float wa = merge_weight(m, mn), wb = merge_weight(m2, mn);
+  l = l * wa + l2 * wb;
+  acc = acc * wa + o2 * wb;
+  m = mn;
 }
 
-// One workgroup per (head, sequence).  (Four workgroups per head, on slices of the head
-// dimension, were slower: each repeats the scattered (m, l) loads.)
+// One workgroup of kMergeThreads per (head, sequence), for any number of partials.  Thread
+// (chunk c, lane q) takes 16-byte chunk c of the head's partial rows in partitions q, q + PL,
+// q + 2 PL, ... (PL lanes) and merges them in that ascending order into a running state;
+// the loads of kMergeBatch partitions are issued together, so a lane's partials arrive in one
+// round trip per kMergeBatch.  The lanes' states are then merged in ascending lane order
+// through LDS.  (A two-stage form -- the maxima first, then the weighted sum -- took three
+// dependent rounds of loads and 8.6 us on the long contexts' 28 MB of partials.)
+constexpr int kMergeThreads = 512;
+constexpr int kMergeBatch = 16;
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attn_reduce_kernel(const AttnArgs a) {
-  constexpr int CHK = D / 4;            // float4 chunks per row
-  constexpr int PL = kThreads / CHK;    // partitions processed side by side
-  extern __shared__ float sm_w[];        // [max_parts] merge weights
-  __shared__ f32x4 sm_acc[kThreads];
-  __shared__ float red[kWaves];
+__global__ __launch_bounds__(kMergeThreads) void attn_reduce_kernel(const AttnArgs a) {
+  constexpr int CH = D / 4;                 // 16-byte chunks of a head's fp32 row: 32 or 16
+  constexpr int PL = kMergeThreads / CH;    // partition lanes: 16 or 32
+  __shared__ float sm_m[PL], sm_l[PL];
+  __shared__ f32x4 sm_acc[PL][CH];
   const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
   const int ctx = a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
-  const int np = (ctx + a.P - 1) / a.P;
-  const size_t base = ((size_t)s * a.Hq + h) * a.max_parts;
-
-  // (m_p, l_p) of this head: entry 2j of item (s, kvh, p)'s line
-  const int kvh = h / a.g, j = h % a.g;
-  const float *ml = a.ws_ml + ((size_t)s * a.Hkv + kvh) * a.max_parts * 32 + 2 * j;
-  float mx = kNegInf;
-  for (int i = tid; i < np; i += kThreads) mx = fmaxf(mx, ml[(size_t)i * 32]);
-  const float M = block_reduce(mx, true, red);
-  float ls = 0.f;
-  for (int i = tid; i < np; i += kThreads) {
-    const float w = merge_weight(ml[(size_t)i * 32], M);
-    sm_w[i] = w;
-    ls += w * ml[(size_t)i * 32 + 1];
-  }
-  const float L = block_reduce(ls, false, red);   // its barriers also publish sm_w
-
-  const int c = tid % CHK, pl = tid / CHK;
+  const int np = min((ctx + a.P - 1) / a.P, a.max_parts);
+  const int kvh = h / a.g, j = h % a.g, c = tid % CH, q = tid / CH;
+  const size_t rs = (size_t)(a.g * D + 32);   // record stride in floats
+  const float *rec = a.ws_rec + ((size_t)s * a.Hkv + kvh) * a.max_parts * rs;
+  float m = kNegInf, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const f32x4 *po = reinterpret_cast<const f32x4 *>(a.ws_o + base * D) + c;
-#pragma unroll 8
-  for (int i = pl; i < np; i += PL) acc += sm_w[i] * po[(size_t)i * CHK];
-  sm_acc[tid] = acc;
-  __syncthreads();
-  if (pl == 0) {
+  for (int p0 = q; p0 < np; p0 += PL * kMergeBatch) {
+    float2 ml[kMergeBatch];
+    f32x4 o[kMergeBatch];
 #pragma unroll
-    for (int q = 1; q < PL; ++q) acc += sm_acc[q * CHK + c];
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int p = p0 + b * PL;
+      const float *r = rec + (size_t)(p < np ? p : 0) * rs;
+      ml[b] = p < np ? *reinterpret_cast<const float2 *>(r + a.g * D + 2 * j) : make_float2(kNegInf, 0.f);
+      o[b] = p < np ? reinterpret_cast<const f32x4 *>(r + j * D)[c] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) lse_merge(m, l, acc, ml[b].x, ml[b].y, o[b]);
+  }
+  if (c == 0) {
+    sm_m[q] = m;
+    sm_l[q] = l;
+  }
+  sm_acc[q][c] = acc;
+  __syncthreads();
+  if (q == 0) {
+    float mt = sm_m[0], lt = sm_l[0];
+    f32x4 at = sm_acc[0][c];
+#pragma unroll
+    for (int r = 1; r < PL; ++r) lse_merge(mt, lt, at, sm_m[r], sm_l[r], sm_acc[r][c]);
     const size_t o = ((size_t)s * a.Hq + h) * D + 4 * c;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<T>(a.out, o + e, acc[e] / L);
+    for (int e = 0; e < 4; ++e) store_out<T>(a.out, o + e, at[e] / lt);
   }
 }
 
 // Pass 2 for at most kShortParts partials per head (the partition count is bounded by the
 // host): a workgroup merges kReduceHeads heads of one sequence, a lane per 16-byte chunk of
-// a head's output, with every partial of the lane loaded at once -- three dependent loads
-// (length, (m, l), partials) per workgroup, and a sixteenth of the workgroups of one per
-// (sequence, head).  Same weights and the same ascending partition order as above.
+// a head's output, with every (m, l) pair and partial of the lane loaded at once -- two
+// dependent rounds of loads (the length, then the records) per workgroup, and a sixteenth of
+// the workgroups of one per (sequence, head).  The maximum first, then the weighted sums, in
+// ascending partition order.
 constexpr int kShortParts = 16;
 constexpr int kReduceHeads = 16;
 template <typename T, int D>
@@ -1599,16 +1605,19 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_short_kernel(const AttnA
   const int h_end = min(a.Hq, (int)(blockIdx.x + 1) * kReduceHeads);
   for (int h = (int)blockIdx.x * kReduceHeads + wv * HPW + lane / CH; h < h_end; h += kWaves * HPW) {
     const int kvh = h / a.g, j = h % a.g;
-    const float *ml = a.ws_ml + ((size_t)s * a.Hkv + kvh) * a.max_parts * 32 + 2 * j;
-    const f32x4 *po = reinterpret_cast<const f32x4 *>(a.ws_o + ((size_t)s * a.Hq + h) * a.max_parts * D) + c;
+    const size_t rs = (size_t)(a.g * D + 32);
+    const float *rec = a.ws_rec + ((size_t)s * a.Hkv + kvh) * a.max_parts * rs;
+    const float *ml = rec + a.g * D + 2 * j;
+    const f32x4 *po = reinterpret_cast<const f32x4 *>(rec + j * D) + c;
     float m[kShortParts], l[kShortParts];
     f32x4 o[kShortParts];
 #pragma unroll
     for (int p = 0; p < kShortParts; ++p) {
       const bool in = p < np;
-      m[p] = in ? ml[(size_t)p * 32] : kNegInf;
-      l[p] = in ? ml[(size_t)p * 32 + 1] : 0.f;
-      o[p] = in ? po[(size_t)p * CH] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      const float2 v = in ? *reinterpret_cast<const float2 *>(ml + (size_t)p * rs) : make_float2(kNegInf, 0.f);
+      m[p] = v.x;
+      l[p] = v.y;
+      o[p] = in ? po[(size_t)p * (rs / 4)] : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     float M = kNegInf;
 #pragma unroll
@@ -1738,7 +1747,7 @@ static void launch_reduce(hipStream_t st, const AttnArgs &a) {
     hipLaunchKernelGGL((attn_reduce_short_kernel<T, D>), grid, dim3(kThreads), 0, st, a);
   } else {
     const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
-    hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kThreads), (size_t)a.max_parts * sizeof(float), st, a);
+    hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kMergeThreads), 0, st, a);
   }
 }
 
@@ -1808,10 +1817,10 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   a.v = v_cache;
   a.tables = block_tables;
   a.ctx = context_lens;
-  const size_t nparts_total = (size_t)num_seqs * num_heads * (size_t)np;
   a.queue = reinterpret_cast<unsigned *>(workspace);
-  a.ws_o = np > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kQueueBytes) : nullptr;
-  a.ws_ml = np > 1 ? a.ws_o + nparts_total * head_dim : nullptr;
+  // records of num_seqs * num_kv_heads * np items: at most what the workspace size counts
+  // (num_seqs * num_heads * np * (head_dim + 32) floats)
+  a.ws_rec = np > 1 ? reinterpret_cast<float *>(reinterpret_cast<char *>(workspace) + kQueueBytes) : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.max_ctx = max_context_len;
   a.Hq = num_heads;
