@@ -117,7 +117,7 @@ def block_stats(cfg, step) -> dict:
 
 
 def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered",
-            block_size: int | None = None, flush_mall: str | None = None):
+            block_size: int | None = None, flush_mall: str | None = None, window: int = 64):
     import torch
     from paged_kv_cache_148_amd import batch, binding
 
@@ -129,6 +129,14 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     if layout == "contiguous":
         # identity free stack: every sequence's blocks are consecutive and ascending
         wl.free_order = list(range(wl.num_blocks))
+    elif layout == "windowed":
+        # shuffled only within windows of `window` consecutive block ids, the windows taken in
+        # ascending order: a sequence's blocks are scattered over spans of `window` blocks only
+        ids = np.arange(wl.num_blocks)
+        rng = np.random.default_rng(cfg.seed + 1000)
+        for i in range(0, wl.num_blocks, window):
+            ids[i:i + window] = rng.permutation(ids[i:i + window])
+        wl.free_order = [int(x) for x in ids[::-1]]
     step = batch.step_for(wl, which)
     bf16 = cfg.dtype == "bf16"
     dev = "cuda"
@@ -244,6 +252,7 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
     nb = algorithmic_bytes(cfg, step)
     res = {
         "workload": name, "step": which, "partition_size": partition, "layout": layout,
+        "window_blocks": window if layout == "windowed" else None,
         "us_per_step": step_s * 1e6, "us_per_step_graph": graph_step_s * 1e6,
         "step_us_events": {"median": float(np.median(step_ms)) * 1e3, "p10": _pct(step_ms, 10) * 1e3,
                            "p90": _pct(step_ms, 90) * 1e3,
@@ -485,9 +494,11 @@ def main():
                     help="only run copy_blocks over 1 GiB (counter calibration for rocprofv3)")
     ap.add_argument("--read-probe", action="store_true",
                     help="only run the plain streaming read over 1 GiB (counter calibration for rocprofv3)")
-    ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous", "head_major"],
-                    help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool; "
-                         "head_major: the shuffled pool in the head-major cache layout")
+    ap.add_argument("--layout", default="scattered", choices=["scattered", "contiguous", "windowed", "head_major"],
+                    help="scattered: seeded shuffled pool (default); contiguous: identity-ordered pool; windowed: "
+                         "shuffled within windows of --window blocks; head_major: the shuffled pool in the "
+                         "head-major cache layout")
+    ap.add_argument("--window", type=int, default=64, help="block ids per window of the windowed layout")
     ap.add_argument("--block-size", type=int, default=None,
                     help="run the workload with this block size instead of its configured one")
     ap.add_argument("--flush-mall", choices=["read", "write"], default=None,
@@ -532,7 +543,7 @@ def main():
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
     res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
-                            args.flush_mall)
+                            args.flush_mall, args.window)
     _say_step(args.workload, res)
     # the CPU oracle on each workload's own inputs, right after its GPU run (all host threads; the
     # line of record's for ~10 s, the others once each; one thread as well on the two smallest)
