@@ -89,9 +89,10 @@ pkv_status paged_kv_write(const void *k_new, const void *v_new, void *k_cache, v
  * pkv_attention_workspace_size -- bytes of device scratch that paged_attention_decode
  * needs: a 256-byte work-queue header, followed, when a sequence can span more than one
  * partition, by the fp32 partial states of the split (given the host-side maximum context
- * length): num_seqs * num_heads * partitions * (head_dim + 32) floats -- the unnormalised
- * partial outputs, then one 128-byte line of (max, sum) pairs per (sequence, KV head,
- * partition), sized as if every head had its own KV head.  Always at least 256.
+ * length): one record per (sequence, partition, KV head) holding the group's unnormalised
+ * partial rows and a 128-byte line of (max, sum) pairs, for which
+ * num_seqs * num_heads * partitions * (head_dim + 32) floats always suffice.  Always at least
+ * 256.
  */
 size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                     int32_t max_context_len, int32_t partition_size);

@@ -73,9 +73,11 @@ struct AttnArgs {
   const void *v;
   const int32_t *tables;
   const int32_t *ctx;
-  float *ws_rec;     // [S, Hkv, max_parts] records of g * D + 32 floats, one per item: the
+  float *ws_rec;     // [S, max_parts, Hkv] records of g * D + 32 floats, one per item: the
                      // group's unnormalised partial rows (head j at j * D), then a 128-byte line
-                     // of (m, l) pairs (head j at 2j, 2j + 1; m in the log2 domain), written whole
+                     // of (m, l) pairs (head j at 2j, 2j + 1; m in the log2 domain), written whole.
+                     // The KV head is fastest, as in the queue's order of full partitions, so the
+                     // records written at about the same time lie side by side.
   int max_blocks;    // table row length
   int max_ctx;       // host bound on ctx
   int Hq, Hkv, g, N;
@@ -246,7 +248,7 @@ __device__ __forceinline__ void finish_group(const AttnArgs &a, int s, int kvh, 
     if (single) {
       store_out<T>(a.out, ((size_t)s * a.Hq + h) * D + d, o / L);
     } else {
-      float *rec = a.ws_rec + (((size_t)s * a.Hkv + kvh) * a.max_parts + p) * (size_t)(g * D + 32);
+      float *rec = a.ws_rec + (((size_t)s * a.max_parts + p) * a.Hkv + kvh) * (size_t)(g * D + 32);
       rec[j * D + d] = o;
       if (d == 0) {
         rec[g * D + 2 * j] = M;
@@ -736,10 +738,11 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
     }
   } else {
     // the item's record, one contiguous piece: the group's partial rows (head j at j * D), then
-    // its (m, l) line (zeros past the group).  Stored as one piece rather than g rows a
-    // partition-stride apart, the partials of a 512-token split cost the long contexts 5-7 us
-    // less (fewer DRAM pages written amid the K/V stream).
-    const size_t item = ((size_t)it.s * a.Hkv + it.kvh) * a.max_parts + it.p;
+    // its (m, l) line (zeros past the group).  Stored as one piece, next to the records of the
+    // items the queue hands out at about the same time, rather than g rows a partition-stride
+    // apart, the 28 MB of partials of the long contexts' 512-token split cost 10 us less amid
+    // the K/V stream (fewer DRAM pages written).
+    const size_t item = ((size_t)it.s * a.max_parts + it.p) * a.Hkv + it.kvh;
     const uint32_t rec_bytes = (uint32_t)(a.g * D + 32) * 4;
     const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.ws_rec + item * (size_t)(a.g * D + 32), rec_bytes);
     if (act) {
@@ -1552,7 +1555,8 @@ __global__ __launch_bounds__(kMergeThreads) void attn_reduce_kernel(const AttnAr
   const int np = min((ctx + a.P - 1) / a.P, a.max_parts);
   const int kvh = h / a.g, j = h % a.g, c = tid % CH, q = tid / CH;
   const size_t rs = (size_t)(a.g * D + 32);   // record stride in floats
-  const float *rec = a.ws_rec + ((size_t)s * a.Hkv + kvh) * a.max_parts * rs;
+  const float *rec = a.ws_rec + ((size_t)s * a.max_parts * a.Hkv + kvh) * rs;
+  const size_t ps = (size_t)a.Hkv * rs;   // between partitions
   float m = kNegInf, l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = q; p0 < np; p0 += PL * kMergeBatch) {
@@ -1561,7 +1565,7 @@ __global__ __launch_bounds__(kMergeThreads) void attn_reduce_kernel(const AttnAr
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int p = p0 + b * PL;
-      const float *r = rec + (size_t)(p < np ? p : 0) * rs;
+      const float *r = rec + (size_t)(p < np ? p : 0) * ps;
       ml[b] = p < np ? *reinterpret_cast<const float2 *>(r + a.g * D + 2 * j) : make_float2(kNegInf, 0.f);
       o[b] = p < np ? reinterpret_cast<const f32x4 *>(r + j * D)[c] : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
@@ -1606,7 +1610,8 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_short_kernel(const AttnA
   for (int h = (int)blockIdx.x * kReduceHeads + wv * HPW + lane / CH; h < h_end; h += kWaves * HPW) {
     const int kvh = h / a.g, j = h % a.g;
     const size_t rs = (size_t)(a.g * D + 32);
-    const float *rec = a.ws_rec + ((size_t)s * a.Hkv + kvh) * a.max_parts * rs;
+    const float *rec = a.ws_rec + ((size_t)s * a.max_parts * a.Hkv + kvh) * rs;
+    const size_t ps = (size_t)a.Hkv * rs;
     const float *ml = rec + a.g * D + 2 * j;
     const f32x4 *po = reinterpret_cast<const f32x4 *>(rec + j * D) + c;
     float m[kShortParts], l[kShortParts];
@@ -1614,10 +1619,10 @@ __global__ __launch_bounds__(kThreads) void attn_reduce_short_kernel(const AttnA
 #pragma unroll
     for (int p = 0; p < kShortParts; ++p) {
       const bool in = p < np;
-      const float2 v = in ? *reinterpret_cast<const float2 *>(ml + (size_t)p * rs) : make_float2(kNegInf, 0.f);
+      const float2 v = in ? *reinterpret_cast<const float2 *>(ml + (size_t)p * ps) : make_float2(kNegInf, 0.f);
       m[p] = v.x;
       l[p] = v.y;
-      o[p] = in ? po[(size_t)p * (rs / 4)] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      o[p] = in ? po[(size_t)p * (ps / 4)] : (f32x4){0.f, 0.f, 0.f, 0.f};
     }
     float M = kNegInf;
 #pragma unroll
@@ -1770,7 +1775,7 @@ extern "C" size_t pkv_attention_workspace_size(int32_t num_seqs, int32_t num_hea
     return kQueueBytes;
   const int64_t np = parts_for(max_context_len, partition_size);
   if (np <= 1) return kQueueBytes;
-  // partial outputs [S, Hq, np, D] and (m, l) lines [S, Hkv, np, 32] (sized for Hkv = Hq)
+  // records of S * Hkv * np items, g * D + 32 floats each: at most S * Hq * np * (D + 32) floats
   return kQueueBytes + (size_t)num_seqs * num_heads * np * (head_dim + 32) * sizeof(float);
 }
 
