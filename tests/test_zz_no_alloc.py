@@ -72,3 +72,32 @@ def test_noalloc_rejects_a_call_beyond_the_scratch():
     with pytest.raises(binding.PkvError) as e:
         binding.paged_attention_decode_noalloc(torch.empty_like(q), q, kc, kc, bt, ctx, 131072, 0.1, 512)
     assert e.value.status == binding.PKV_ERR_SCRATCH_LIMIT
+
+
+def test_noalloc_captured_in_a_hip_graph():
+    # the use the entry point exists for: captured once in a HIP graph (it allocates nothing) and
+    # replayed, with eager calls on the same static scratch between the replays; every replay and
+    # every eager call gives paged_attention_decode's output bit for bit
+    import torch
+    name, P = "gqa70b", 512
+    wl, step, d = _case(name, P, 16)
+    want, _ = _both(wl, step, d, P)
+    out = torch.full_like(d["out"], float("nan"))
+    other = torch.empty_like(d["out"])
+    graph = torch.cuda.CUDAGraph()
+    print("[gpu case] noalloc graph capture", name, "P", P, flush=True)
+    with torch.cuda.graph(graph):
+        binding.paged_attention_decode_noalloc(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                               d["context_lens"], step.max_context_len, wl.scale, P)
+    for rep in range(3):
+        print("[gpu case] noalloc graph replay", rep, flush=True)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert H.bits(out).tobytes() == want.tobytes(), f"replay {rep}"
+        binding.paged_attention_decode_noalloc(other, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                               d["context_lens"], step.max_context_len, wl.scale, P)
+        torch.cuda.synchronize()
+        assert H.bits(other).tobytes() == want.tobytes(), f"eager after replay {rep}"
+    del graph
