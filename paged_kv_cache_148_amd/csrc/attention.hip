@@ -1785,7 +1785,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
                          int32_t max_context_len, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale, int32_t partition_size,
                          void *workspace, size_t workspace_bytes, pkv_dtype dtype, void *stream,
-                         const void *k_new = nullptr, const void *v_new = nullptr) {
+                         const void *k_new = nullptr, const void *v_new = nullptr, bool check_only = false) {
   const bool fuse = k_new != nullptr || v_new != nullptr;
   if (dtype != PKV_DTYPE_F32 && dtype != PKV_DTYPE_BF16) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1 ||
@@ -1814,6 +1814,7 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   if (np > kMaxReduceParts) return PKV_ERR_UNSUPPORTED;
   const size_t need = pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return PKV_ERR_INVALID_ARG;
+  if (check_only) return PKV_OK;
 
   AttnArgs a;
   a.out = out;
@@ -1991,8 +1992,14 @@ extern "C" pkv_status paged_attention_decode_noalloc(void *out, const void *q, c
   if (pkv_attention_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size) >
       kStaticScratchBytes)
     return PKV_ERR_SCRATCH_LIMIT;
-  void *ws = nullptr;
-  const pkv_status st = static_scratch((hipStream_t)stream, &ws);
+  // every other host check of paged_attention_decode next, with an aligned stand-in for the scratch
+  // that is never dereferenced: a rejected call enqueues nothing, not even the first call's clear
+  void *ws = reinterpret_cast<void *>(uintptr_t{256});
+  pkv_status st = decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                         max_context_len, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                         partition_size, ws, kStaticScratchBytes, dtype, stream, nullptr, nullptr, true);
+  if (st != PKV_OK || num_seqs == 0) return st;
+  st = static_scratch((hipStream_t)stream, &ws);
   if (st != PKV_OK) return st;
   return decode(false, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, partition_size, ws,

@@ -170,3 +170,16 @@ def test_noalloc_rejects_beyond_its_static_scratch_on_the_host(L):
     st = L.paged_attention_decode_noalloc(None, None, None, None, None, 8192, None, 0, 64, 64, 8, 128, 16, 4,
                                           0.1, 512, PKV_DTYPE_BF16, None)
     assert st == PKV_ERR_INVALID_ARG                                     # max_context_len 0
+
+
+def test_noalloc_checks_its_arguments_before_touching_the_device(L):
+    # a rejected call enqueues nothing and looks nothing up: with no GPU here, a call whose only
+    # fault is a null pointer (or a bad shape) must come back INVALID_ARG / UNSUPPORTED, not a HIP
+    # error from the scratch lookup; an empty batch is a no-op
+    dummy = 256   # aligned, never dereferenced: the call is rejected first
+    args = lambda q, S=4, B=16, Hq=8, Hkv=2: (dummy, q, dummy, dummy, dummy, 64, dummy, 1000, S, Hq, Hkv, 128, B, 100,
+                                              0.1, 0, PKV_DTYPE_BF16, None)
+    assert L.paged_attention_decode_noalloc(*args(None)) == PKV_ERR_INVALID_ARG
+    assert L.paged_attention_decode_noalloc(*args(dummy, Hq=9, Hkv=2)) == PKV_ERR_INVALID_ARG
+    assert L.paged_attention_decode_noalloc(*args(dummy, B=24)) == PKV_ERR_UNSUPPORTED
+    assert L.paged_attention_decode_noalloc(*args(dummy, S=0)) == PKV_OK
