@@ -135,6 +135,13 @@ pkv_path pkv_attention_path(int32_t num_heads, int32_t num_kv_heads, int32_t hea
  * Device values: context_lens[s] <= 0 gives out[s] = 0; context_lens[s] >
  * max_context_len, or a table entry read that lies outside [0, num_blocks), gives
  * NaN for the affected outputs.  Neither faults.
+ *
+ * Work items: on the bf16 / head_dim 128 paths with blocks of 16 slots or more, a large
+ * launch whose sequences' blocks lie far apart in the pool hands out the bulk of its work as
+ * items of 2 or 4 KV heads (the library decides per launch; see attention.hip).  The item
+ * width changes no bit of any output.  The environment variable PKV_WIDE_ITEMS=1, 2 or 4
+ * caps the width and applies it to every item of the launch (1: one KV head per item), for
+ * tests and tuning.
  */
 pkv_status paged_attention_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
                                   const int32_t *block_tables, int32_t max_blocks_per_seq,

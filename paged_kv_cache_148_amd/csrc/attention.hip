@@ -10,7 +10,12 @@
 //
 // Work unit: one (KV head, context partition, sequence) item, processed by one
 // workgroup of 4 waves.  An item serves every query head of the KV head's group, so each
-// K/V byte is read once per group.  Without a partition size the partition is the whole
+// K/V byte is read once per group.  On the tile paths the bulk of a large launch goes out in
+// wide items of 2 or 4 adjacent KV heads of one (sequence, partition): the workgroup's waves
+// then read the same blocks at the same time (one address translation serves several waves,
+// which halves the translation misses of a pool scattered over gigabytes), and each head's
+// tiles are still accumulated and merged exactly as in a one-head item, so the width changes
+// no bit of the result.  Without a partition size the partition is the whole
 // context.  With one, an item leaves a partial state (running max m, sum l, unnormalised
 // o) as one contiguous record in the workspace and a second kernel merges the partials by
 // log-sum-exp;
@@ -40,6 +45,7 @@
 // Scores carry scale * log2(e) so every exponential is a hardware exp2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -65,6 +71,14 @@ constexpr int kMaxReduceParts = 8192;    // partials per (sequence, head) a call
 constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
 constexpr int kClasses = 16;            // length classes of the longest-first schedule
 constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the workspace
+// Wide work items (tile paths, row layout): at least kWideMinItems of them per workgroup, and the
+// queue's last kWideReserve one-head items per workgroup stay one head wide (the finer tail).
+constexpr int kWideMinItems = 4;
+constexpr int kWideReserve = 4;
+// ... and only where the sampled consecutive blocks of the sequences lie this far apart (in one
+// pool): on pools shuffled within windows of 32 MB one-head items were faster, within 256 MB and
+// beyond wide ones (long contexts, 512-token partitions).
+constexpr int64_t kWideFarBytes = 64ll << 20;
 
 struct AttnArgs {
   void *out;
@@ -73,9 +87,10 @@ struct AttnArgs {
   const void *v;
   const int32_t *tables;
   const int32_t *ctx;
-  float *ws_rec;     // [S, max_parts, Hkv] records of g * D + 32 floats, one per item: the
-                     // group's unnormalised partial rows (head j at j * D), then a 128-byte line
-                     // of (m, l) pairs (head j at 2j, 2j + 1; m in the log2 domain), written whole.
+  float *ws_rec;     // [S, max_parts, Hkv] records of g * D + 32 floats, one per (sequence,
+                     // partition, KV head): the group's unnormalised partial rows (head j at j * D),
+                     // then a 128-byte line of (m, l) pairs (head j at 2j, 2j + 1; m in the log2
+                     // domain; the rest of the line unused).
                      // The KV head is fastest, as in the queue's order of full partitions, so the
                      // records written at about the same time lie side by side.
   int max_blocks;    // table row length
@@ -90,6 +105,9 @@ struct AttnArgs {
   float cls_scale;   // length classes of the longest-first schedule: kClasses / (min(P, max_ctx) + 1)
   const void *k_new; // [S, Hkv, D]: each sequence's new K row, stored at position ctx - 1 by the
   const void *v_new; //   item that attends to it (the fused write; null otherwise)
+  int hpi;           // tile path: KV heads of a wide work item (1, 2 or 4)
+  int reserve;       // tile path: the queue's last `reserve` one-head items are not widened
+  int far_blocks;    // tile path: block-id distance of "far apart" blocks (0: wide items regardless)
 };
 
 // Work-item order across the chip.  Workgroups go round-robin to the 8 XCDs by their
@@ -314,10 +332,14 @@ struct TileSmem {
 
 // One work item as a wave sees it.  Every field is wave-uniform.
 struct MItem {
-  int s, p, kvh;
+  int s, p, kvh;   // kvh: this wave's KV head
+  int kvh0, u;     // the item's first KV head; kvh = kvh0 + u
+  int width;       // KV heads of the item (1, 2 or 4); kWaves / width waves per KV head
+  int ph0, pst;    // this wave's first tile phase and the stride between its phases
+  int b1, b2, b3;  // loop indices where this wave's 2nd, 3rd, 4th phase begins (kBig: none)
   int t0, t1;    // attended token range [t0, t1)
   int tile_lo;   // first 16-token tile of the partition
-  int n_my;      // this wave's live tiles: tile_lo + wave + kWaves * i, i < n_my
+  int n_my;      // this wave's live tiles (loop indices i < n_my; tile_of)
   int n_pad;     // loop length: n_my rounded up to a multiple of NB, at least NB
   int fill;      // 0 attend; 1 write zeros; 2 write NaN; 3 nothing to do
   int single;    // the partition is the whole context: normalise into out
@@ -333,7 +355,9 @@ struct MItem {
 // LDS (dynamic): pref[S] (inclusive prefix of full-partition items), ctx[S], order[S].
 struct LptSched {
   int total_full;   // items of the full partitions
-  int total;        // all items
+  int total;        // all items (one KV head each)
+  int nwide;        // the first nwide * hpi of them go out as nwide items of hpi KV heads each
+  int items;        // queue entries: nwide + total - nwide * hpi
 };
 
 // Scratch of the schedule build: sequences go in chunks of 64 (one per lane).
@@ -581,17 +605,34 @@ __device__ __forceinline__ WorkItem decode_lpt(int w, const LptSched &sc, const 
   return it;
 }
 
+constexpr int kBig = 1 << 30;   // "no such phase": past every loop index
+
+// Tile phases: phase q of an item is its tiles q, q + 4, q + 8, ...  A one-head item gives wave w
+// phase w.  A wide item (width 2 or 4 KV heads) gives each KV head kWaves / width waves, and
+// each of them several phases, one after the other: wave (u, ph0) streams phases ph0,
+// ph0 + pst, ... of KV head kvh0 + u, storing its state at each phase's end.  Every phase of
+// every head is then accumulated exactly as in a one-head item and the merge is the same, so
+// the width changes no bit of the result; it puts the waves of a workgroup on the same
+// blocks at the same time.
 template <int NB>
-__device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int kvh, int ctx, int wave) {
+__device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int kvh, int ctx, int wave,
+                                           int width) {
   MItem it;
+  const int wph = kWaves / width;
   it.s = s;
   it.p = p;
-  it.kvh = kvh;
+  it.kvh0 = kvh;
+  it.u = wave / wph;
+  it.kvh = kvh + it.u;
+  it.width = width;
+  it.ph0 = wave % wph;
+  it.pst = wph;
   it.tile_lo = (p * a.P) >> 4;
   it.t0 = p * a.P;
   it.t1 = 0;
   it.n_my = 0;
   it.single = 0;
+  int nt = 0;
   if (ctx < 1 || ctx > a.max_ctx) {
     it.fill = p == 0 ? (ctx < 1 ? 1 : 2) : 3;
   } else if (p * a.P >= ctx) {
@@ -600,20 +641,30 @@ __device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int 
     it.fill = 0;
     it.t1 = min(p * a.P + a.P, ctx);
     it.single = ctx <= a.P;
-    const int nt = ((it.t1 + 15) >> 4) - it.tile_lo;
-    it.n_my = nt > wave ? (nt - wave + kWaves - 1) / kWaves : 0;
+    nt = ((it.t1 + 15) >> 4) - it.tile_lo;
   }
+  // tiles of phase q: nt > q ? (nt - q + 3) / 4 : 0
+  int c[kWaves];
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const int q = it.ph0 + k * wph;
+    c[k] = k < width && nt > q ? (nt - q + kWaves - 1) / kWaves : 0;
+  }
+  it.b1 = width > 1 ? c[0] : kBig;
+  it.b2 = width > 2 ? c[0] + c[1] : kBig;
+  it.b3 = width > 3 ? c[0] + c[1] + c[2] : kBig;
+  it.n_my = c[0] + c[1] + c[2] + c[3];
   it.n_pad = max(NB, (it.n_my + NB - 1) / NB * NB);
   return it;
 }
 
-// An empty item: what the stream holds past the workgroup's last item.
-__device__ __forceinline__ MItem no_item() {
-  MItem it;
-  it.s = it.p = it.kvh = it.t0 = it.t1 = it.tile_lo = it.n_my = it.single = 0;
-  it.n_pad = 0;
-  it.fill = 3;
-  return it;
+// Tile (index within the sequence) of this wave's loop index i.
+template <bool WIDE>
+__device__ __forceinline__ int tile_of(const MItem &it, int i) {
+  if constexpr (!WIDE) return it.tile_lo + it.ph0 + kWaves * i;
+  const int k = (i >= it.b1) + (i >= it.b2) + (i >= it.b3);
+  const int start = k == 0 ? 0 : k == 1 ? it.b1 : k == 2 ? it.b2 : it.b3;
+  return it.tile_lo + it.ph0 + k * it.pst + kWaves * (i - start);
 }
 
 // Blocks that one 16-token tile spans: 16 / B for blocks of 4 or 8 slots, else 1.
@@ -622,19 +673,18 @@ constexpr int tile_blocks() { return B < 16 ? 16 / B : 1; }
 
 // Block-table entries of tiles 64c .. 64c + 63 of an item, one per lane: entry h of each
 // tile's blocks (zero past the table row or for an item with nothing to attend).
-template <int B>
-__device__ __forceinline__ int table_chunk(const AttnArgs &a, const MItem &it, int c, int h, int wave, int lane) {
+template <int B, bool WIDE>
+__device__ __forceinline__ int table_chunk(const AttnArgs &a, const MItem &it, int c, int h, int lane) {
   const bool live = it.fill == 0 && 64 * c < it.n_my;
   const __amdgpu_buffer_rsrc_t r =
       buf_rsrc(a.tables + (size_t)it.s * a.max_blocks, live ? (uint32_t)a.max_blocks * 4u : 0u);
-  const int tok = (it.tile_lo + wave + kWaves * (64 * c + lane)) << 4;
+  const int tok = tile_of<WIDE>(it, 64 * c + lane) << 4;
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (tok / B + h) * 4, 0, 0);
 }
-template <int B>
-__device__ __forceinline__ void table_chunks(const AttnArgs &a, const MItem &it, int c, int wave, int lane,
-                                             int *tb) {
+template <int B, bool WIDE>
+__device__ __forceinline__ void table_chunks(const AttnArgs &a, const MItem &it, int c, int lane, int *tb) {
 #pragma unroll
-  for (int h = 0; h < tile_blocks<B>(); ++h) tb[h] = table_chunk<B>(a, it, c, h, wave, lane);
+  for (int h = 0; h < tile_blocks<B>(); ++h) tb[h] = table_chunk<B, WIDE>(a, it, c, h, lane);
 }
 
 // The Q^T operand of an item: head c16 of the KV head's group (zero columns past g).
@@ -665,6 +715,14 @@ __device__ __forceinline__ MItem uniform(MItem it) {
   it.s = __builtin_amdgcn_readfirstlane(it.s);
   it.p = __builtin_amdgcn_readfirstlane(it.p);
   it.kvh = __builtin_amdgcn_readfirstlane(it.kvh);
+  it.kvh0 = __builtin_amdgcn_readfirstlane(it.kvh0);
+  it.u = __builtin_amdgcn_readfirstlane(it.u);
+  it.width = __builtin_amdgcn_readfirstlane(it.width);
+  it.ph0 = __builtin_amdgcn_readfirstlane(it.ph0);
+  it.pst = __builtin_amdgcn_readfirstlane(it.pst);
+  it.b1 = __builtin_amdgcn_readfirstlane(it.b1);
+  it.b2 = __builtin_amdgcn_readfirstlane(it.b2);
+  it.b3 = __builtin_amdgcn_readfirstlane(it.b3);
   it.t0 = __builtin_amdgcn_readfirstlane(it.t0);
   it.t1 = __builtin_amdgcn_readfirstlane(it.t1);
   it.tile_lo = __builtin_amdgcn_readfirstlane(it.tile_lo);
@@ -675,28 +733,52 @@ __device__ __forceinline__ MItem uniform(MItem it) {
   return it;
 }
 
-template <int NB>
+template <int NB, bool WIDE>
 __device__ __forceinline__ MItem item_at(const AttnArgs &a, int w, const LptSched &sc, const int *sm_pref,
                                          const int *sm_ctx, const int *sm_order, int wave) {
-  const int total = sc.total;
-  if (w >= total) return no_item();
-  if (a.persistent) {
-    const WorkItem wi = decode_lpt(w, sc, sm_pref, sm_ctx, sm_order, a);
-    return uniform(make_item<NB>(a, wi.s, wi.p, wi.kvh, sm_ctx[wi.s], wave));
+  // one make_item on every path (the item's fields stay in registers)
+  int s = 0, p = 0, kvh = 0, ctx = 1, width = 1;
+  const bool none = w >= sc.items;
+  if (!none) {
+    if (a.persistent) {
+      const bool wide = w < sc.nwide;
+      const int r = wide ? w * a.hpi : sc.nwide * a.hpi + (w - sc.nwide);
+      const WorkItem wi = decode_lpt(r, sc, sm_pref, sm_ctx, sm_order, a);
+      s = wi.s;
+      p = wi.p;
+      kvh = wi.kvh;
+      ctx = sm_ctx[wi.s];
+      width = WIDE && wide ? a.hpi : 1;
+    } else {
+      kvh = w % a.Hkv;
+      p = (w / a.Hkv) % a.max_parts;
+      s = w / (a.Hkv * a.max_parts);
+      ctx = a.ctx[s];
+    }
   }
-  const int kvh = w % a.Hkv, p = (w / a.Hkv) % a.max_parts, s = w / (a.Hkv * a.max_parts);
-  return uniform(make_item<NB>(a, s, p, kvh, a.ctx[s], wave));
+  MItem it = make_item<NB>(a, s, p, kvh, ctx, wave, width);
+  if (none) {   // what the stream holds past the workgroup's last item
+    it.fill = 3;
+    it.t1 = 0;
+    it.n_my = 0;
+    it.n_pad = 0;
+    it.single = 0;
+  }
+  return uniform(it);
 }
 
-// Merge of the four waves' states of an item, then its output (normalised, or a partial
-// state for the second pass).  Thread t covers head t / 16 of the group and head dims
-// 8 (t % 16) .. +7: ten independent LDS reads and one wait, then 16-byte stores.
+// Merge of the four phase states of each head of an item, then its output (normalised, or a
+// partial state for the second pass).  Thread t covers row t / 16 of the item's query heads
+// (the KV heads' groups one after the other) and head dims 8 (t % 16) .. +7: ten independent
+// LDS reads and one wait, then 16-byte stores.
 __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
                                             const float (*sm_l)[kWaves], const float (*sm_o)[16][kTileOS],
                                             const int *sm_bad) {
   constexpr int D = 128;
   const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 8;
-  const bool act = j < a.g;   // heads past the group: their (unwritten) LDS rows are read, not used
+  // row j: query head j of the item's heads (head jj of KV head kvh0 + u)
+  const int u = j / a.g, jj = j - u * a.g;
+  const bool act = u < it.width;   // rows past the item's heads: their LDS rows are read, not used
   const f32x4 m4 = *reinterpret_cast<const f32x4 *>(sm_m[j]);
   const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sm_l[j]);
   f32x4 olo[kWaves], ohi[kWaves];
@@ -723,9 +805,9 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
     L = __builtin_nanf("");
     lo = hi = (f32x4){L, L, L, L};
   }
-  // the group's first head h0: every store below goes through one wave-uniform descriptor
-  // based there, with a 32-bit per-lane offset
-  const size_t h0 = (size_t)it.s * a.Hq + (size_t)it.kvh * a.g;
+  // the item's first head h0: every store below goes through one wave-uniform descriptor
+  // based there, with a 32-bit per-lane offset (the item's KV heads are adjacent)
+  const size_t h0 = (size_t)it.s * a.Hq + (size_t)it.kvh0 * a.g;
   if (it.single) {
     if (act) {
       u32x4 v;
@@ -733,7 +815,8 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
       v[1] = pack_bf16x2(lo[2] / L, lo[3] / L);
       v[2] = pack_bf16x2(hi[0] / L, hi[1] / L);
       v[3] = pack_bf16x2(hi[2] / L, hi[3] / L);
-      const __amdgpu_buffer_rsrc_t ro = buf_rsrc(reinterpret_cast<uint16_t *>(a.out) + h0 * D, (uint32_t)(a.g * D * 2));
+      const __amdgpu_buffer_rsrc_t ro =
+          buf_rsrc(reinterpret_cast<uint16_t *>(a.out) + h0 * D, (uint32_t)(it.width * a.g * D * 2));
       __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((j * D + d0) * 2), 0, kStoreSc1);
     }
   } else {
@@ -742,20 +825,18 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
     // items the queue hands out at about the same time, rather than g rows a partition-stride
     // apart, the 28 MB of partials of the long contexts' 512-token split cost 10 us less amid
     // the K/V stream (fewer DRAM pages written).
-    const size_t item = ((size_t)it.s * a.max_parts + it.p) * a.Hkv + it.kvh;
+    const size_t item = ((size_t)it.s * a.max_parts + it.p) * a.Hkv + it.kvh0;
     const uint32_t rec_bytes = (uint32_t)(a.g * D + 32) * 4;
-    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.ws_rec + item * (size_t)(a.g * D + 32), rec_bytes);
+    const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.ws_rec + item * (size_t)(a.g * D + 32), it.width * rec_bytes);
+    const uint32_t rec = (uint32_t)u * rec_bytes;   // the record of KV head kvh0 + u
     if (act) {
-      const uint32_t off = (uint32_t)(j * D + d0) * 4;
+      const uint32_t off = rec + (uint32_t)(jj * D + d0) * 4;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), ro, off, 0, kStoreSc1);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), ro, off + 16, 0, kStoreSc1);
-    }
-    const float M1 = __shfl_down(M, 16), L1 = __shfl_down(L, 16);   // head j + 1 is lane t + 16
-    if ((t & 31) == 0) {
-      const bool act1 = j + 1 < a.g;
-      const f32x4 v = {act ? M : 0.f, act ? L : 0.f, act1 ? M1 : 0.f, act1 ? L1 : 0.f};
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, (uint32_t)(a.g * D + 2 * j) * 4, 0,
-                                             kStoreSc1);
+      if ((t & 15) == 0) {   // the head's (m, l) pair
+        const u32x2 v = {__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, L)};
+        __builtin_amdgcn_raw_buffer_store_b64(v, ro, rec + (uint32_t)(a.g * D + 2 * jj) * 4, 0, kStoreSc1);
+      }
     }
   }
 }
@@ -773,8 +854,9 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
 // meet q and P in fp32 FMAs on exactly widened elements, and q.k is summed over a 16-lane row
 // by DPP (an MFMA would leave 15 of its 16 columns empty).
 // FUSE: the fused write of each sequence's new token (row layout only; see load_item_new).
-template <int B, int NB, bool HM, bool MF, bool FUSE = false>
+template <int B, int NB, bool HM, bool MF, bool FUSE = false, bool WIDE = false>
 __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
+  static_assert(!WIDE || (!HM && B >= 16), "wide items: row layout, blocks of 16 slots or more");
   static_assert(!HM || B >= 16, "the head-major path takes blocks of 16 slots or more");
   static_assert(!FUSE || !HM, "the fused write is built for the row layout");
   static_assert(NB >= 2, "the ring holds the tile being computed and at least one ahead");
@@ -791,6 +873,26 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   // items, so a fixed split costs little balance, and the launch makes no queue fetch), then
   // one index per queue fetch, counted from 2 * gridDim.x.  The fetch for it_{k+2} is made
   // while it_k runs, so both the current and the next item are always known.
+  // Wide items pay where the sequences' blocks lie far apart (a pool scattered over hundreds of
+  // MB: address translation then bounds the stream); on a pool whose consecutive blocks lie close
+  // together one-head items stream faster.  Each wave samples 64 pairs of consecutive table
+  // entries (lane l: entries l / S and l / S + 1 of sequence l % S), loaded with the lengths
+  // before the schedule build, and the launch goes wide where most sampled pairs of blocks
+  // that a sequence uses lie at least far_blocks apart (every workgroup sees the same bits).
+  int smp_ctx = 0, smp_t0 = 0, smp_t1 = 0;
+  const int smp_s = lane % a.S, smp_j = lane / a.S;
+  const bool smp_in = smp_j + 1 < a.max_blocks;
+  if constexpr (WIDE) {
+    if (a.far_blocks > 0) {
+      // (per-lane addresses: plain loads; a buffer descriptor's base must be the same in every lane)
+      const int32_t *row = a.tables + (size_t)smp_s * a.max_blocks;
+      if (smp_in) {
+        smp_t0 = row[smp_j];
+        smp_t1 = row[smp_j + 1];
+      }
+      smp_ctx = a.ctx[smp_s];
+    }
+  }
   LptSched sched;
   if (a.persistent) {
     sched = build_lpt_schedule(a, sm_pref, sm_ctx, sm_order, sched_sm);   // ends with a barrier
@@ -798,11 +900,23 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     sched.total_full = 0;
     sched.total = (int)gridDim.x;
   }
-  const int total = sched.total;
+  bool go_wide = WIDE && a.persistent && a.hpi > 1;
+  if constexpr (WIDE) {
+    if (a.far_blocks > 0) {
+      const bool valid = smp_in && smp_ctx <= a.max_ctx && smp_ctx > (smp_j + 1) * B;
+      const int64_t gap = (int64_t)smp_t1 - (int64_t)smp_t0;
+      const bool far = valid && (gap >= a.far_blocks || gap <= -(int64_t)a.far_blocks);
+      go_wide = go_wide && 2 * __popcll(__ballot(far)) > __popcll(__ballot(valid));
+    }
+  }
+  // the queue's bulk goes out in wide items, its last `reserve` one-head items as they are
+  sched.nwide = go_wide ? max(0, sched.total - a.reserve) / a.hpi : 0;
+  sched.items = sched.nwide + sched.total - sched.nwide * a.hpi;
+  const int total = sched.items;
   int w = (int)blockIdx.x;
   int wn = a.persistent ? (int)(gridDim.x + blockIdx.x) : total;
   if (w < total) {
-    MItem cur = item_at<NB>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
+    MItem cur = item_at<NB, WIDE>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
     MItem nxt;
 
     // Token of a tile row.  Load instruction r gives lane group grp the tile token
@@ -824,8 +938,8 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     // one after it; next item: its first two; one register per block of a tile), q operands,
     // validity flags
     int tb_cur[BPT], tb_ahead[BPT], tb_next[BPT], tb_next_ahead[BPT];
-    table_chunks<B>(a, cur, 0, wave, lane, tb_cur);
-    table_chunks<B>(a, cur, 1, wave, lane, tb_ahead);
+    table_chunks<B, WIDE>(a, cur, 0, lane, tb_cur);
+    table_chunks<B, WIDE>(a, cur, 1, lane, tb_ahead);
     // q operands: MF, head c16 of the group in the B layout; !MF on the head-major layout, the
     // item's head at the K chunks lane group grp holds (dims 32c + 8grp); !MF on the row
     // layout, dims 8 c16 .. + 7
@@ -864,7 +978,9 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     auto new_tile = [&](const MItem &it) -> int {
       if (!FUSE || !is_last(it)) return -1;
       const int rel = ((it.t1 - 1) >> 4) - it.tile_lo;
-      return rel % kWaves == wave ? rel / kWaves : -1;
+      const int q = rel & (kWaves - 1), k = q / it.pst;
+      if (q - k * it.pst != it.ph0) return -1;
+      return (k == 0 ? 0 : k == 1 ? it.b1 : k == 2 ? it.b2 : it.b3) + (rel >> 2);
     };
     // the table entry of the new token's block is taken when its tile is issued (-1: outside
     // the pool, so the row is not stored); hn: that block among the tile's
@@ -881,7 +997,7 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     // Loads of tile i of an item (zero-range descriptors past its live tiles).
     auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
       const bool live = i < it.n_my;
-      const int tok0 = (it.tile_lo + wave + kWaves * i) << 4;
+      const int tok0 = tile_of<WIDE>(it, i) << 4;
       if constexpr (HM) {
         constexpr uint32_t hb_bytes = D * B * 2;   // one (block, KV head) of K or of V
         const size_t off = ((size_t)phys[0] * a.Hkv + it.kvh) * hb_bytes;
@@ -923,9 +1039,9 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
       if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
 #pragma unroll
         for (int h = 0; h < BPT; ++h) tb_cur[h] = tb_ahead[h];
-        table_chunks<B>(a, cur, (i >> 6) + 1, wave, lane, tb_ahead);
+        table_chunks<B, WIDE>(a, cur, (i >> 6) + 1, lane, tb_ahead);
       }
-      const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      const int tok0 = tile_of<WIDE>(cur, i) << 4;
       int phys[BPT];
       if constexpr (FUSE) {
 #pragma unroll
@@ -944,7 +1060,7 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     };
     // tile i (< NB - 1) of the next item
     auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
-      const int tok0 = (nxt.tile_lo + wave + kWaves * i) << 4;
+      const int tok0 = tile_of<WIDE>(nxt, i) << 4;
       int phys[BPT];
       if constexpr (FUSE) {
 #pragma unroll
@@ -970,9 +1086,77 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     f32x4 acc[NACC];
 #pragma unroll
     for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    int mbuf = 0;   // the current item's merge buffer
+    auto reset_state = [&]() {
+      m = kNegInf;
+      lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    };
+    // This wave's state of one phase into merge buffer mb, slot `slot`, rows of its KV head:
+    // (m, l) of each head and its unnormalised rows; the item's sum is spread over the lane
+    // groups except on the head-major VALU path.
+    auto store_state = [&](int mb, int slot) {
+      float lh = lsum;
+      if constexpr (MF || !HM) {
+        lh += __shfl_xor(lh, 16);
+        lh += __shfl_xor(lh, 32);
+      }
+      const int row = WIDE ? cur.u * a.g + c16 : c16;     // MF: head c16 of this wave's group
+      const bool own = !WIDE || c16 < a.g;                // (one-head items write all 16 rows)
+      const int urow = WIDE ? cur.u : 0;                  // !MF: the wave's one head
+      if constexpr (MF) {
+        if (grp == 0 && own) {
+          sm.m[mb][row][slot] = m;
+          sm.l[mb][row][slot] = lh;
+        }
+      } else if (lane == 0) {   // one head: m is the same in every lane
+        sm.m[mb][urow][slot] = m;
+        sm.l[mb][urow][slot] = lh;
+      }
+      if constexpr (!MF) {   // the lane groups' sums, then dims 8 c16 .. + 7 from lane group 0
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = acc[i][e];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[i][e] = x;
+          }
+        }
+        if (grp == 0) {
+          if constexpr (HM) {   // dims 16j + c16
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sm.o[mb][slot][urow][16 * j + c16] = acc[j >> 2][j & 3];
+          } else {              // dims 8 c16 .. + 7
+            *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16]) = acc[0];
+            *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16 + 4]) = acc[1];
+          }
+        }
+      } else if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
+        if (own) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][row][16 * i + 4 * grp]) = acc[i];
+        }
+      } else if (own) {     // MFMA i holds dims 32grp + 8r + i
+        float *dst = &sm.o[mb][slot][row][32 * grp];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
+        }
+      }
+    };
 
     auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
-      const int tok0 = (cur.tile_lo + wave + kWaves * i) << 4;
+      if constexpr (WIDE) {
+        if (i == cur.b1 || i == cur.b2 || i == cur.b3) {   // a phase of a wide item ends
+          store_state(mbuf, cur.ph0 + (i == cur.b1 ? 0 : i == cur.b2 ? 1 : 2) * cur.pst);
+          reset_state();
+        }
+      }
+      const int tok0 = tile_of<WIDE>(cur, i) << 4;
       if constexpr (FUSE) {
         if (i == new_i_cur) {
           // the new token's place in the tile, and the load (lane group, instruction) of it
@@ -1168,12 +1352,13 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
 
     for (int k = 0;; ++k) {
+      mbuf = k & 1;
       // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
       // copies into the current item's registers at the end of this iteration, so those
       // copies never wait on memory.
-      nxt = item_at<NB>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
-      table_chunks<B>(a, nxt, 0, wave, lane, tb_next);
-      table_chunks<B>(a, nxt, 1, wave, lane, tb_next_ahead);
+      nxt = item_at<NB, WIDE>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
+      table_chunks<B, WIDE>(a, nxt, 0, lane, tb_next);
+      table_chunks<B, WIDE>(a, nxt, 1, lane, tb_next_ahead);
       load_item_q(nxt, qnext);
       load_item_new(nxt, kn_nxt, vn_nxt);
       new_i_nxt = new_tile(nxt);
@@ -1214,61 +1399,26 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
         if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
       }
 
-      // merge the waves' states of it_k (the next item's first loads are in flight); the item's
-      // sum is spread over the lane groups except on the head-major VALU path
-      float lh = lsum;
-      if constexpr (MF || !HM) {
-        lh += __shfl_xor(lh, 16);
-        lh += __shfl_xor(lh, 32);
-      }
+      // the waves' states of it_k into the merge buffer (the next item's first loads are in
+      // flight): the phase in progress, then empty states for a wide item's phases with no tiles
       const int mb = k & 1;
-      if constexpr (MF) {
-        if (grp == 0) {
-          sm.m[mb][c16][wave] = m;
-          sm.l[mb][c16][wave] = lh;
+      if constexpr (WIDE) {
+        const int kcur = (cur.n_my > cur.b1) + (cur.n_my > cur.b2) + (cur.n_my > cur.b3);
+        store_state(mb, cur.ph0 + kcur * cur.pst);
+        for (int kk = kcur + 1; kk < cur.width; ++kk) {
+          reset_state();
+          store_state(mb, cur.ph0 + kk * cur.pst);
         }
-      } else if (lane == 0) {   // one head: m is the same in every lane
-        sm.m[mb][0][wave] = m;
-        sm.l[mb][0][wave] = lh;
+      } else {
+        store_state(mb, wave);
       }
       if (lane == 0) sm.bad[mb][wave] = bad_cur;
-      if constexpr (!MF) {   // the lane groups' sums, then dims 8 c16 .. + 7 from lane group 0
-#pragma unroll
-        for (int i = 0; i < NACC; ++i) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float x = acc[i][e];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            acc[i][e] = x;
-          }
-        }
-        if (grp == 0) {
-          if constexpr (HM) {   // dims 16j + c16
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sm.o[mb][wave][0][16 * j + c16] = acc[j >> 2][j & 3];
-          } else {              // dims 8 c16 .. + 7
-            *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][0][8 * c16]) = acc[0];
-            *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][0][8 * c16 + 4]) = acc[1];
-          }
-        }
-      } else if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][wave][c16][16 * i + 4 * grp]) = acc[i];
-      } else {              // MFMA i holds dims 32grp + 8r + i
-        float *dst = &sm.o[mb][wave][c16][32 * grp];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
-        }
-      }
       if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(2 * gridDim.x + fetched) : total;
       __syncthreads();
       if (cur.fill == 0)
         tile_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
       else if (cur.fill != 3)
-        fill_group<uint16_t, D>(a, cur.s, cur.kvh * a.g, a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
+        fill_group<uint16_t, D>(a, cur.s, cur.kvh0 * a.g, cur.width * a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
       if (wn >= total) break;
 
       // advance the stream by one item
@@ -1693,7 +1843,15 @@ static Pass1Fn vec_fn(int g, int B) {
 }
 
 template <bool MF, int NB, bool FUSE = false>
-static Pass1Fn tile_fn(int B) {
+static Pass1Fn tile_fn(int B, bool wide) {
+  if (wide) {
+    switch (B) {
+      case 16: return attn_tile_kernel<16, NB, false, MF, FUSE, true>;
+      case 32: return attn_tile_kernel<32, NB, false, MF, FUSE, true>;
+      case 64: return attn_tile_kernel<64, NB, false, MF, FUSE, true>;
+      default: return attn_tile_kernel<128, NB, false, MF, FUSE, true>;
+    }
+  }
   switch (B) {
     case 4: return attn_tile_kernel<4, NB, false, MF, FUSE>;
     case 8: return attn_tile_kernel<8, NB, false, MF, FUSE>;
@@ -1718,17 +1876,19 @@ static Pass1Fn tile_hm_fn(int B) {
 // query head per KV head keeps the shallow ring: its merge and stores are a single head's.
 // fuse: the fused write of the new tokens (row layout, tile paths, shallow ring: the new rows
 // take the registers the deep ring would need).
-static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major, bool deep, bool fuse) {
+static Pass1Fn pass1_fn(pkv_path path, pkv_dtype dt, int D, int B, int g, bool head_major, bool deep, bool fuse,
+                        bool wide) {
   if (fuse) {
-    return path == PKV_PATH_MFMA ? tile_fn<true, kTileDepthShallow, true>(B)
-                                 : tile_fn<false, kTileDepthShallow, true>(B);
+    return path == PKV_PATH_MFMA ? tile_fn<true, kTileDepthShallow, true>(B, wide)
+                                 : tile_fn<false, kTileDepthShallow, true>(B, wide);
   }
   if (head_major) {
     if (path == PKV_PATH_TILE_VALU) return tile_hm_fn<false, kTileDepthShallow>(B);
     return deep ? tile_hm_fn<true, kTileDepthDeep>(B) : tile_hm_fn<true, kTileDepthShallow>(B);
   }
-  if (path == PKV_PATH_MFMA) return deep ? tile_fn<true, kTileDepthDeep>(B) : tile_fn<true, kTileDepthShallow>(B);
-  if (path == PKV_PATH_TILE_VALU) return tile_fn<false, kTileDepthShallow>(B);
+  if (path == PKV_PATH_MFMA)
+    return deep ? tile_fn<true, kTileDepthDeep>(B, wide) : tile_fn<true, kTileDepthShallow>(B, wide);
+  if (path == PKV_PATH_TILE_VALU) return tile_fn<false, kTileDepthShallow>(B, wide);
   if (dt == PKV_DTYPE_BF16) return D == 128 ? vec_fn<uint16_t, 128>(g, B) : vec_fn<uint16_t, 64>(g, B);
   return D == 128 ? vec_fn<float, 128>(g, B) : vec_fn<float, 64>(g, B);
 }
@@ -1742,6 +1902,23 @@ static int resident_workgroups(Pass1Fn fn, size_t dyn_lds) {
       hipSuccess)
     return 0;
   return (occ > 0 ? occ : 1) * cus;
+}
+
+// KV heads per wide work item.  The widest of 4 and 2 heads that divides Hkv, whose query
+// heads fit the 16 rows of the merge (width * g <= 16) and that still leaves at least
+// kWideMinItems wide items per workgroup (items_ub: one-head items if every partition were
+// non-empty); 1 (no wide items) otherwise.  PKV_WIDE_ITEMS=1, 2 or 4 in the environment caps the
+// width instead and makes every item of the launch that wide (*forced; for tests and tuning: the
+// results are the same bits at every width).
+static int wide_heads(int Hkv, int g, int64_t items_ub, int64_t grid, bool *forced) {
+  const char *e = getenv("PKV_WIDE_ITEMS");
+  const int cap = e && *e ? atoi(e) : 0;
+  *forced = cap > 0;
+  for (int h = 4; h >= 2; h /= 2) {
+    if (Hkv % h != 0 || h * g > 16) continue;
+    if (cap > 0 ? h <= cap : items_ub / h >= kWideMinItems * grid) return h;
+  }
+  return 1;
 }
 
 // Pass 2: the short-count kernel when every head has at most kShortParts partials.
@@ -1840,6 +2017,9 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
   a.cls_scale = (float)kClasses / (float)((P < max_context_len ? P : max_context_len) + 1);
   a.k_new = k_new;
   a.v_new = v_new;
+  a.hpi = 1;
+  a.reserve = 0;
+  a.far_blocks = 0;
 
   hipStream_t st = (hipStream_t)stream;
   const int64_t items = np * num_kv_heads * (int64_t)num_seqs;   // upper bound: every partition non-empty
@@ -1859,8 +2039,8 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
     if (ws != PKV_OK) return ws;
     a.k_new = a.v_new = nullptr;
   }
-  const Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, deep, fuse_in_tiles);
   // persistent workgroups when the schedule fits in LDS, else one workgroup per possible item
+  Pass1Fn fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, deep, fuse_in_tiles, false);
   size_t dyn_lds = 0;
   int64_t grid = items;
   a.persistent = 0;
@@ -1872,6 +2052,19 @@ static pkv_status decode(bool head_major, void *out, const void *q, const void *
       grid = items < resident ? items : resident;
     } else {
       dyn_lds = 0;
+    }
+  }
+  // wide work items on the tile paths of the row layout
+  if (a.persistent && path != PKV_PATH_VECTOR && !head_major && block_size >= 16) {
+    bool forced = false;
+    a.hpi = wide_heads(num_kv_heads, a.g, items, grid, &forced);
+    if (a.hpi > 1) {
+      fn = pass1_fn(path, dtype, head_dim, block_size, a.g, head_major, deep, fuse_in_tiles, true);
+      const int resident = resident_workgroups(fn, dyn_lds);
+      if (resident > 0 && resident < grid) grid = resident;
+      a.reserve = forced ? 0 : (int)(kWideReserve * grid);
+      const int64_t blk_bytes = (int64_t)block_size * num_kv_heads * head_dim * (bf16 ? 2 : 4);
+      a.far_blocks = forced ? 0 : (int)((kWideFarBytes + blk_bytes - 1) / blk_bytes);
     }
   }
   void *args[] = {&a};

@@ -954,3 +954,122 @@ def test_fused_write_bad_values_write_nothing():
     for s_ in (1, 4, 5):
         assert H.bits(e["out"])[s_].tobytes() == H.bits(d["out"])[s_].tobytes()
 
+
+
+# ---------------------------------------------------------------------------
+# wide work items: every width gives the same bits
+# ---------------------------------------------------------------------------
+
+def _attend(monkeypatch, wl, step, d, P, width):
+    """paged_attention_decode with every work item `width` KV heads wide (PKV_WIDE_ITEMS; None:
+    the library's own choice), on the inputs in d; returns the output's bits."""
+    import torch
+    if width is None:
+        monkeypatch.delenv("PKV_WIDE_ITEMS", raising=False)
+    else:
+        monkeypatch.setenv("PKV_WIDE_ITEMS", str(width))
+    out = torch.empty_like(d["q"])
+    binding.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                   step.max_context_len, wl.scale, P)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("PKV_WIDE_ITEMS", raising=False)
+    return H.bits(out).copy()
+
+
+@pytest.mark.parametrize("name,P,widths", [("long_splitk", 512, (1, 2, 4)), ("mha7b", 0, (1, 2, 4)),
+                                           ("gqa70b", 2048, (1, 2))])
+def test_wide_items_same_bits_full_size(monkeypatch, name, P, widths):
+    # the library's choice (wide items for the bulk of these launches, one-head items at the
+    # queue's end) and every forced width give the output of one-head items bit for bit
+    wl = _wl(name)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P, do_attn=False)
+    _say("wide items", name, "P", P)
+    base = _attend(monkeypatch, wl, step, d, P, 1)
+    for width in (None,) + widths[1:]:
+        got = _attend(monkeypatch, wl, step, d, P, width)
+        assert got.tobytes() == base.tobytes(), f"{name}: width {width}"
+    _, _, _, ref = H.oracle_step(wl, "steady", P)
+    H.check_close(got, ref, "bf16", f"{name} width {widths[-1]} P={P}")
+
+
+WIDE_SHAPES = [
+    # S, Hq, Hkv, B, ctx range, partition sizes
+    (5, 8, 8, 16, (1, 700), (0, 64)),        # g = 1 (VALU dots)
+    (4, 16, 8, 32, (1, 900), (0, 128)),      # g = 2
+    (4, 24, 8, 32, (1, 400), (0, 128)),      # g = 3: a KV head's rows straddle the waves' rows
+    (6, 32, 8, 16, (1, 1300), (0, 512)),     # g = 4, the deep ring
+    (3, 64, 8, 64, (1, 2600), (0, 256)),     # g = 8, B = 64, more than 64 tiles per wave
+    (4, 32, 8, 128, (1, 1000), (0, 512)),    # g = 4, B = 128
+    (3, 12, 4, 16, (4000, 9000), (1024,)),   # g = 3, long partitions (shallow ring)
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=[f"g{s[1] // s[2]}-B{s[3]}" for s in WIDE_SHAPES])
+def test_wide_items_same_bits(monkeypatch, shape):
+    # every item of the launch 2 or 4 KV heads wide (all that the group allows), against one-head
+    # items: the same bits, ragged contexts (1 token included) and the oracle's tolerance
+    S, Hq, Hkv, B, (lo, hi), parts = shape
+    cfg = workloads.Config("wide", "bf16", S, Hq, Hkv, 128, B, ("uniform", lo, hi), seed=50 + Hq + B)
+    wl = workloads.make_workload(cfg)
+    wl.context_lens[0] = 1
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, 0, do_attn=False)
+    g = Hq // Hkv
+    widths = [w for w in (2, 4) if Hkv % w == 0 and w * g <= 16]
+    assert widths
+    for P in parts:
+        _say("wide items", shape, "P", P)
+        base = _attend(monkeypatch, wl, step, d, P, 1)
+        for width in widths:
+            got = _attend(monkeypatch, wl, step, d, P, width)
+            assert got.tobytes() == base.tobytes(), f"width {width} P={P}"
+        _, _, _, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(base, ref, "bf16", f"{shape} P={P}")
+
+
+@pytest.mark.parametrize("name,num_seqs,P", [("gqa70b", 12, 256), ("mha7b", 6, 0), ("long_splitk", None, 512)])
+def test_wide_items_fused_write_same_bits(monkeypatch, name, num_seqs, P):
+    # the fused write inside wide items: caches and output bit for bit those of one-head items
+    import torch
+    wl = _fused_wl(name, num_seqs)
+    step = pbatch.step_for(wl)
+    res = {}
+    g = wl.cfg.num_heads // wl.cfg.num_kv_heads
+    for width in [1] + [w for w in (2, 4) if wl.cfg.num_kv_heads % w == 0 and w * g <= 16]:
+        _say("wide fused", name, "P", P, "width", width)
+        monkeypatch.setenv("PKV_WIDE_ITEMS", str(width))
+        d = H.upload(wl, step)
+        binding.paged_attention_decode_write(d["out"], d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"],
+                                             d["block_tables"], d["context_lens"], step.max_context_len, wl.scale, P)
+        torch.cuda.synchronize()
+        res[width] = [H.bits(d[k]).tobytes() for k in ("out", "k_cache", "v_cache")]
+    monkeypatch.delenv("PKV_WIDE_ITEMS", raising=False)
+    for width, r in res.items():
+        assert r == res[1], f"width {width}"
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_wide_items_bad_values(monkeypatch, P):
+    # unusable lengths and table entries inside wide items: zeros / NaN for those sequences (every
+    # KV head of them), the other sequences as with one-head items
+    import torch
+    wl = _wl("gqa70b", num_seqs=40)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P, do_attn=False)
+    ctx = d["context_lens"].clone()
+    ctx[0] = 0
+    ctx[2] = step.max_context_len + 5
+    d["block_tables"][1, 0] = wl.num_blocks + 1000
+    d["context_lens"] = ctx
+    _say("wide bad values", "P", P)
+    base = _attend(monkeypatch, wl, step, d, P, 1)
+    got = _attend(monkeypatch, wl, step, d, P, 2)
+    o = H.widen(got)
+    assert (o[0] == 0).all()
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all()
+    assert got.tobytes() == base.tobytes()
+    del torch
