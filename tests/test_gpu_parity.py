@@ -607,7 +607,17 @@ def test_bad_device_values_give_defined_outputs(num_seqs, P):
 # scheduling: persistent work queue and the large-batch fallback
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name,P", [("gqa70b", 512), ("mha7b", 0), ("tiny_fp32", 8)])
+# The merge of partial states inside the first launch (its own workgroups merging once their
+# items are done, no second kernel) was built and taken out again: its first GPU run of the
+# partition-64 GQA case did not finish within the test's time limit, twice (a stale poll of the
+# arrival counters was found and fixed between the two runs; the second cause was not found).
+# These cases stay here, skipped, for whoever takes it up again.
+MERGE_INSIDE_SKIP = pytest.mark.skip(reason="merge inside the first launch: taken out after two GPU runs "
+                                            "of its first case did not finish")
+
+
+@pytest.mark.parametrize("name,P", [("gqa70b", 512), ("mha7b", 0), ("tiny_fp32", 8),
+                                    pytest.param("gqa70b", 64, marks=MERGE_INSIDE_SKIP)])
 def test_work_queue_counters_return_to_zero(name, P):
     import torch
     wl = _wl(name, num_seqs=min(12, workloads.CONFIGS[name].num_seqs))
@@ -1073,3 +1083,81 @@ def test_wide_items_bad_values(monkeypatch, P):
     assert np.isnan(o[1]).all() and np.isnan(o[2]).all()
     assert got.tobytes() == base.tobytes()
     del torch
+
+
+# ---------------------------------------------------------------------------
+# the merge of partial states inside the first launch: the same bits as the second kernel
+# ---------------------------------------------------------------------------
+
+def _attend_env(monkeypatch, wl, step, d, P, env):
+    import torch
+    for k in ("PKV_MERGE_PASS", "PKV_WIDE_ITEMS"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    out = torch.empty_like(d["q"])
+    binding.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                                   step.max_context_len, wl.scale, P)
+    torch.cuda.synchronize()
+    for k in env:
+        monkeypatch.delenv(k, raising=False)
+    return H.bits(out).copy()
+
+
+MERGE_CASES = [
+    # workload, sequences or contexts, partition size
+    ("long_splitk", None, 512),                                   # full size: 64 .. 256 partitions
+    ("long_splitk", np.array([32768, 5000, 12345, 1, 700, 513], np.int64), 256),   # ragged, single-partition ones
+    ("gqa70b", 24, 64),                                           # g = 8, > 16 partitions per head
+    ("mha7b", 8, 64),                                             # g = 1 (VALU dots)
+]
+
+
+@MERGE_INSIDE_SKIP
+@pytest.mark.parametrize("name,seqs,P", MERGE_CASES, ids=[f"{c[0]}-P{c[2]}-{i}" for i, c in enumerate(MERGE_CASES)])
+def test_merge_inside_launch_same_bits(monkeypatch, name, seqs, P):
+    # merged by the first launch's own workgroups (the default here) against the second kernel
+    # (PKV_MERGE_PASS=1), with one-head and wide items: bit for bit, and the oracle's tolerance
+    if isinstance(seqs, np.ndarray):
+        wl = _wl(name, ctx=seqs)
+    else:
+        wl = _wl(name, num_seqs=seqs)
+    step = pbatch.step_for(wl)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P, do_attn=False)
+    _say("merge inside", name, "P", P)
+    base = _attend_env(monkeypatch, wl, step, d, P, {"PKV_MERGE_PASS": "1", "PKV_WIDE_ITEMS": "1"})
+    for env in ({}, {"PKV_WIDE_ITEMS": "1"}, {"PKV_WIDE_ITEMS": "2"}, {"PKV_MERGE_PASS": "1"}):
+        got = _attend_env(monkeypatch, wl, step, d, P, env)
+        assert got.tobytes() == base.tobytes(), f"{env}"
+    _, _, _, ref = H.oracle_step(wl, "steady", P)
+    H.check_close(base, ref, "bf16", f"merge inside {name} P={P}")
+
+
+@MERGE_INSIDE_SKIP
+def test_merge_inside_launch_reused_workspace():
+    # one workspace for calls on different inputs and shapes in a row, each merged inside the
+    # launch: every output against the oracle (records of an earlier call at the same addresses
+    # must not be read), and the first inputs again give the first call's bits
+    import torch
+    P = 256
+    wla = _wl("long_splitk", ctx=np.array([9000, 5000, 12345, 700], np.int64))
+    wlb = _wl("long_splitk", ctx=np.array([12000, 4100, 300, 8000, 6000], np.int64), seed=11)
+    steps = [pbatch.step_for(w) for w in (wla, wlb)]
+    need = max(binding.attention_workspace_size(w.cfg.num_seqs, w.cfg.num_heads, w.cfg.head_dim, st.max_context_len, P)
+               for w, st in zip((wla, wlb), steps))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for wl, step in ((wla, steps[0]), (wlb, steps[1]), (wla, steps[0])):
+        _say("merge inside, reused workspace", wl.cfg.num_seqs)
+        d = H.upload(wl, step)
+        H.gpu_step(wl, step, d, P, do_attn=False)
+        binding.paged_attention_decode(d["out"], d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                       d["context_lens"], step.max_context_len, wl.scale, P, ws)
+        torch.cuda.synchronize()
+        assert not ws[:8].any().item()
+        got = H.bits(d["out"]).copy()
+        _, _, _, ref = H.oracle_step(wl, "steady", P)
+        H.check_close(got, ref, "bf16", f"reused workspace S={wl.cfg.num_seqs}")
+        outs.append(got)
+    assert outs[2].tobytes() == outs[0].tobytes()
