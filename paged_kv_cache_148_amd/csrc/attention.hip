@@ -769,13 +769,17 @@ __device__ __forceinline__ MItem item_at(const AttnArgs &a, int w, const LptSche
 
 // Merge of the four phase states of each head of an item, then its output (normalised, or a
 // partial state for the second pass).  Thread t covers row t / 16 of the item's query heads
-// (the KV heads' groups one after the other) and head dims 8 (t % 16) .. +7: ten independent
-// LDS reads and one wait, then 16-byte stores.
+// (the KV heads' groups one after the other) and head dims 4l .. 4l + 3 and 64 + 4l .. +3
+// (l = t % 16): ten independent LDS reads and one wait.  Each store instruction then writes
+// whole 256-byte runs of a head's row (16 lanes, consecutive 16-byte pieces), so every line of
+// the write-through partial states is written at once: with each lane's 8 consecutive dims
+// instead, an instruction left every 32-byte sector half written and the memory side counted
+// twice the records' bytes.
 __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
                                             const float (*sm_l)[kWaves], const float (*sm_o)[16][kTileOS],
                                             const int *sm_bad) {
   constexpr int D = 128;
-  const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 8;
+  const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 4, d1 = 64 + d0;
   // row j: query head j of the item's heads (head jj of KV head kvh0 + u)
   const int u = j / a.g, jj = j - u * a.g;
   const bool act = u < it.width;   // rows past the item's heads: their LDS rows are read, not used
@@ -785,7 +789,7 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     olo[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d0]);
-    ohi[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d0 + 4]);
+    ohi[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d1]);
   }
   const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
   float M = kNegInf;
@@ -810,14 +814,12 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
   const size_t h0 = (size_t)it.s * a.Hq + (size_t)it.kvh0 * a.g;
   if (it.single) {
     if (act) {
-      u32x4 v;
-      v[0] = pack_bf16x2(lo[0] / L, lo[1] / L);
-      v[1] = pack_bf16x2(lo[2] / L, lo[3] / L);
-      v[2] = pack_bf16x2(hi[0] / L, hi[1] / L);
-      v[3] = pack_bf16x2(hi[2] / L, hi[3] / L);
+      const u32x2 vlo = {pack_bf16x2(lo[0] / L, lo[1] / L), pack_bf16x2(lo[2] / L, lo[3] / L)};
+      const u32x2 vhi = {pack_bf16x2(hi[0] / L, hi[1] / L), pack_bf16x2(hi[2] / L, hi[3] / L)};
       const __amdgpu_buffer_rsrc_t ro =
           buf_rsrc(reinterpret_cast<uint16_t *>(a.out) + h0 * D, (uint32_t)(it.width * a.g * D * 2));
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (uint32_t)((j * D + d0) * 2), 0, kStoreSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(vlo, ro, (uint32_t)((j * D + d0) * 2), 0, kStoreSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(vhi, ro, (uint32_t)((j * D + d1) * 2), 0, kStoreSc1);
     }
   } else {
     // the item's record, one contiguous piece: the group's partial rows (head j at j * D), then
@@ -830,9 +832,9 @@ __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, 
     const __amdgpu_buffer_rsrc_t ro = buf_rsrc(a.ws_rec + item * (size_t)(a.g * D + 32), it.width * rec_bytes);
     const uint32_t rec = (uint32_t)u * rec_bytes;   // the record of KV head kvh0 + u
     if (act) {
-      const uint32_t off = rec + (uint32_t)(jj * D + d0) * 4;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), ro, off, 0, kStoreSc1);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), ro, off + 16, 0, kStoreSc1);
+      const uint32_t off = rec + (uint32_t)(jj * D) * 4;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), ro, off + d0 * 4, 0, kStoreSc1);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), ro, off + d1 * 4, 0, kStoreSc1);
       if ((t & 15) == 0) {   // the head's (m, l) pair
         const u32x2 v = {__builtin_bit_cast(uint32_t, M), __builtin_bit_cast(uint32_t, L)};
         __builtin_amdgcn_raw_buffer_store_b64(v, ro, rec + (uint32_t)(a.g * D + 2 * jj) * 4, 0, kStoreSc1);
