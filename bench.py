@@ -117,7 +117,7 @@ def block_stats(cfg, step) -> dict:
 
 
 def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layout: str = "scattered",
-            block_size: int | None = None, flush_mall: str | None = None, window: int = 64):
+            block_size: int | None = None, flush_mall: str | None = None, window: int = 64, keep: bool = False):
     import torch
     from paged_kv_cache_148_amd import batch, binding
 
@@ -280,6 +280,12 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
         unique_tokens = shared + int((step.context_lens.astype(np.int64) - shared).sum())
         res["unique_kv_bytes"] = unique_tokens * 2 * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
         res["note"] = "unique KV fits the 256 MB Infinity Cache: logical GB/s is not an HBM figure"
+    if keep and not hm:
+        # what the step left on the GPU (every timed call repeats the same step on the same state,
+        # so this is one step's result): the output and both pools, as raw bits, for the parity
+        # report of the CPU oracle's leg
+        res["_results"] = {"out": batch.from_torch_bits(out), "k_cache": batch.from_torch_bits(kc),
+                           "v_cache": batch.from_torch_bits(vc)}
     del q, kc, vc, kn, vn, out, ws
     torch.cuda.empty_cache()
     return res, wl, step
@@ -435,30 +441,74 @@ def stream_read_ceiling(steps: int = 20, gib: int = 2) -> dict:
             "frac_of_peak": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(wl, step, partition: int, budget_s: float = 10.0, threads: int = 0, max_reps: int = 200) -> dict:
+def cpu_baseline(wl, which: str, partition: int, budget_s: float = 10.0, threads: int = 0, max_reps: int = 200,
+                 gpu_results: dict | None = None) -> dict:
     """The CPU oracle on the same inputs: whole decode steps (copies, write, attention) on the
-    host, `threads` OpenMP threads (0: all it may use), repeated until about budget_s seconds have
-    been spent (at least once, at most max_reps times)."""
+    host with the oracle's own step inputs (its block model on the workload's free stack),
+    `threads` OpenMP threads (0: all it may use), repeated until about budget_s seconds have been
+    spent (at least once, at most max_reps times).  With gpu_results (the GPU step's output and
+    pools as raw bits), the last step's results are compared with them: "parity"."""
     import oracle
+    from oracle import batch as obatch
     cfg = wl.cfg
-    nb = algorithmic_bytes(cfg, step)
+    o = obatch.step_for(wl, which)
+    nb = algorithmic_bytes(cfg, _StepBytes(o))
     nt = threads if threads > 0 else oracle.max_threads()
     reps, t_total = 0, 0.0
+    kc = vc = ref = None
     while reps == 0 or (t_total < budget_s and reps < max_reps):
+        kc = vc = ref = None   # the previous step's pool copies go before the next are made
         kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
         t = time.perf_counter()
-        oracle.copy_blocks(kc, vc, step.copy_pairs)
-        oracle.kv_write(wl.k_new, wl.v_new, kc, vc, step.slot_mapping)
-        oracle.attention(wl.q, kc, vc, step.block_tables, step.context_lens, wl.scale, partition, num_threads=nt)
+        oracle.copy_blocks(kc, vc, o["copy_pairs"])
+        oracle.kv_write(wl.k_new, wl.v_new, kc, vc, o["slot_mapping"])
+        ref = oracle.attention(wl.q, kc, vc, o["block_tables"], o["context_lens"], wl.scale, partition, num_threads=nt)
         t_total += time.perf_counter() - t
         reps += 1
-        del kc, vc
     per = t_total / reps
-    return {"value": round(nb["step"] / per / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
-            "us_per_step": round(per * 1e6, 1), "steps_timed": reps, "seconds": round(t_total, 2),
-            "sample": f"{reps} whole decode step(s) of the {cfg.name} workload ({cfg.num_seqs} seqs, "
-                      f"{int(step.context_lens.sum())} tokens, partition {partition}), fp64 scalar C, "
-                      f"{nt} OpenMP thread(s), {t_total:.1f} s in all"}
+    res = {"value": round(nb["step"] / per / 1e9, 3), "unit": "GB/s", "cores": nt, "kind": "oracle",
+           "us_per_step": round(per * 1e6, 1), "steps_timed": reps, "seconds": round(t_total, 2),
+           "sample": f"{reps} whole decode step(s) of the {cfg.name} workload ({cfg.num_seqs} seqs, "
+                     f"{int(o['context_lens'].sum())} tokens, partition {partition}), fp64 scalar C, "
+                     f"{nt} OpenMP thread(s), {t_total:.1f} s in all"}
+    if gpu_results is not None:
+        res["parity"] = parity(gpu_results, ref, kc, vc, cfg.dtype)
+    return res
+
+
+class _StepBytes:
+    """The fields of a step that algorithmic_bytes reads, from the oracle's step dict."""
+
+    def __init__(self, o):
+        self.context_lens, self.block_tables = o["context_lens"], o["block_tables"]
+        self.slot_mapping, self.copy_pairs = o["slot_mapping"], o["copy_pairs"]
+
+
+# The parity tests' tolerance: bf16 inputs with fp32 accumulation, max |gpu - ref| <= 2e-2; fp32
+# inputs, |gpu - ref| <= 1e-5 + 1e-4 |ref| per element.
+BF16_MAX_ABS = 2e-2
+F32_ABS, F32_REL = 1e-5, 1e-4
+
+
+def parity(gpu: dict, ref, kc, vc, dtype: str) -> dict:
+    """Every output element against the fp64 oracle (max-abs, max-rel, within the tolerance), and
+    both pools after the step's copies and write, bit for bit."""
+    import oracle
+    g = oracle.widen(gpu["out"]).reshape(ref.shape)
+    err = np.abs(g - ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    max_rel = float((err / np.maximum(np.abs(ref), 1e-30)).max()) if err.size else 0.0
+    if dtype == "f32":
+        ok = bool((err <= F32_ABS + F32_REL * np.abs(ref)).all())
+        tol = f"|gpu - ref| <= {F32_ABS:g} + {F32_REL:g} |ref| per element"
+    else:
+        ok = max_abs <= BF16_MAX_ABS
+        tol = f"max |gpu - ref| <= {BF16_MAX_ABS:g}"
+    return {"outputs_compared": int(err.size), "max_abs": float(f"{max_abs:.3e}"), "max_rel": float(f"{max_rel:.3e}"),
+            "within_tolerance": bool(ok and np.isfinite(g).all()), "tolerance": tol,
+            "k_cache_bit_exact": bool(np.array_equal(gpu["k_cache"], kc)),
+            "v_cache_bit_exact": bool(np.array_equal(gpu["v_cache"], vc)),
+            "reference": "CPU oracle (fp64), its own step inputs from the same free stack"}
 
 
 def host_info() -> dict:
@@ -543,13 +593,13 @@ def main():
                           "kernel_source_hash": kernel_source_hash()}), flush=True)
         return
     res, wl, step = run_gpu(args.workload, which, args.steps, args.warmup, main_part, args.layout, args.block_size,
-                            args.flush_mall, args.window)
+                            args.flush_mall, args.window, keep=not args.no_cpu)
     _say_step(args.workload, res)
     # the CPU oracle on each workload's own inputs, right after its GPU run (all host threads; the
     # line of record's for ~10 s, the others once each; one thread as well on the two smallest)
     cpu_runs = {}
     if not args.no_cpu:
-        cpu_runs[args.workload] = cpu_baseline(wl, step, main_part, budget_s=10.0)
+        cpu_runs[args.workload] = cpu_baseline(wl, which, main_part, budget_s=10.0, gpu_results=res.pop("_results", None))
         _say_cpu(args.workload, cpu_runs[args.workload])
     del wl, step
     others = {}
@@ -560,14 +610,15 @@ def main():
                 continue
             for w in (["fork", "steady"] if name == "fork_cow" else ["steady"]):
                 key = f"{name}/{w}" if name == "fork_cow" else name
-                r, wl_o, step_o = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall)
+                r, wl_o, step_o = run_gpu(name, w, args.steps, args.warmup, PARTITION[name], flush_mall=args.flush_mall,
+                                          keep=not args.no_cpu)
                 others[key] = r
                 _say_step(key, r)
                 if not args.no_cpu:
-                    cpu_runs[key] = cpu_baseline(wl_o, step_o, PARTITION[name], budget_s=0.0)
+                    cpu_runs[key] = cpu_baseline(wl_o, w, PARTITION[name], budget_s=0.0, gpu_results=r.pop("_results", None))
                     _say_cpu(key, cpu_runs[key])
                     if name in SINGLE_THREAD:
-                        single[key] = cpu_baseline(wl_o, step_o, PARTITION[name], budget_s=0.0, threads=1)
+                        single[key] = cpu_baseline(wl_o, w, PARTITION[name], budget_s=0.0, threads=1)
                         _say_cpu(key + " (1 thread)", single[key])
                 del wl_o, step_o
 
@@ -578,6 +629,7 @@ def main():
     cpu = None
     if cpu_runs:
         cpu = dict(cpu_runs[args.workload])
+        cpu.pop("parity", None)
         cpu["host"] = host_info()
         cpu["per_workload"] = {k: {kk: v[kk] for kk in ("value", "unit", "us_per_step", "cores", "steps_timed")}
                                for k, v in cpu_runs.items()}
@@ -587,6 +639,7 @@ def main():
     for k, v in others.items():
         e = {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
         e["roofline"] = roofline(k.split("/")[0], v, rd)
+        e["parity"] = cpu_runs.get(k, {}).get("parity")
         workloads_out[k] = e
     line = {
         "metric": METRIC,
@@ -617,6 +670,7 @@ def main():
                                 "p10": round(res["attention_us_events_p10"], 2),
                                 "p90": round(res["attention_us_events_p90"], 2)},
         "cpu_baseline": cpu,
+        "parity": cpu_runs.get(args.workload, {}).get("parity"),
         "workloads": workloads_out,
         "movers": mv,
         "stream_read": rd,
@@ -639,6 +693,11 @@ def _say_step(name, r):
 def _say_cpu(name, c):
     print(f"[bench] CPU oracle {name}: {c['us_per_step']:.0f} us/step, {c['value']:.2f} GB/s, {c['cores']} thread(s), "
           f"{c['steps_timed']} step(s)", file=sys.stderr, flush=True)
+    pr = c.get("parity")
+    if pr:
+        print(f"[bench] parity {name}: {pr['outputs_compared']} outputs, max_abs {pr['max_abs']:.3e}, "
+              f"max_rel {pr['max_rel']:.3e}, within tolerance {pr['within_tolerance']}, pools bit-exact "
+              f"{pr['k_cache_bit_exact'] and pr['v_cache_bit_exact']}", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

@@ -73,3 +73,51 @@ def test_cpu_baseline_on_the_tiny_workload():
     c = bench.cpu_baseline(wl, step, 0, budget_s=0.0, threads=1)
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["steps_timed"] == 1 and c["value"] > 0
     assert "tiny_fp32" in c["sample"]
+
+
+def _bf16_bits(x):
+    """fp64 -> bf16 bit patterns, round to nearest even (finite values)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _oracle_results(wl, which, partition):
+    import oracle
+    from oracle import batch as obatch
+    o = obatch.step_for(wl, which)
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+    oracle.copy_blocks(kc, vc, o["copy_pairs"])
+    oracle.kv_write(wl.k_new, wl.v_new, kc, vc, o["slot_mapping"])
+    ref = oracle.attention(wl.q, kc, vc, o["block_tables"], o["context_lens"], wl.scale, partition)
+    return ref, kc, vc
+
+
+def test_oracle_leg_reports_parity_fp32():
+    import workloads
+    wl = workloads.make_workload("tiny_fp32")
+    ref, kc, vc = _oracle_results(wl, "steady", 0)
+    good = {"out": ref.astype(np.float32), "k_cache": kc.copy(), "v_cache": vc.copy()}
+    r = bench.cpu_baseline(wl, "steady", 0, budget_s=0.0, gpu_results=good)
+    p = r["parity"]
+    assert p["outputs_compared"] == ref.size and p["within_tolerance"]
+    assert p["k_cache_bit_exact"] and p["v_cache_bit_exact"] and p["max_abs"] < 1e-6
+    bad_out = dict(good, out=good["out"].copy())
+    bad_out["out"].flat[7] += 1e-3                       # one element past 1e-5 + 1e-4 |ref|
+    assert not bench.cpu_baseline(wl, "steady", 0, budget_s=0.0, gpu_results=bad_out)["parity"]["within_tolerance"]
+    bad_pool = dict(good, v_cache=good["v_cache"].copy())
+    bad_pool["v_cache"].view(np.uint32).flat[123] ^= 1   # one bit of one V element
+    p = bench.cpu_baseline(wl, "steady", 0, budget_s=0.0, gpu_results=bad_pool)["parity"]
+    assert p["k_cache_bit_exact"] and not p["v_cache_bit_exact"] and p["within_tolerance"]
+
+
+def test_oracle_leg_reports_parity_bf16_fork_step():
+    import workloads
+    wl = workloads.make_workload("fork_cow")
+    ref, kc, vc = _oracle_results(wl, "fork", 1024)
+    good = {"out": _bf16_bits(ref), "k_cache": kc.copy(), "v_cache": vc.copy()}
+    p = bench.cpu_baseline(wl, "fork", 1024, budget_s=0.0, gpu_results=good)["parity"]
+    assert p["within_tolerance"] and p["k_cache_bit_exact"] and p["v_cache_bit_exact"]
+    assert 0 < p["max_abs"] < 2e-2                       # the output's own bf16 rounding
+    stale = dict(good, k_cache=wl.k_cache.copy())       # the pool before the step's copies and write
+    p = bench.cpu_baseline(wl, "fork", 1024, budget_s=0.0, gpu_results=stale)["parity"]
+    assert not p["k_cache_bit_exact"] and p["v_cache_bit_exact"]
