@@ -1693,15 +1693,27 @@ __device__ __forceinline__ void lse_merge(float &m, float &l, f32x4 &acc, float 
 // round trip per kMergeBatch.  The lanes' states are then merged in ascending lane order
 // through LDS.  (A two-stage form -- the maxima first, then the weighted sum -- took three
 // dependent rounds of loads and 8.6 us on the long contexts' 28 MB of partials.)
+//
+// Workgroup i of a one-dimensional grid runs on XCD i % 8 (workgroups are dealt to the eight
+// XCDs in turn), and takes (sequence, head) number v, where the workgroups of one XCD take
+// consecutive v: the g heads of a KV head, whose (m, l) pairs share one 128-byte line of each
+// record, then read that line through one L2 instead of g.  Beyond 2^32 threads in one
+// dimension the grid is (head, sequence) instead.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeBatch = 16;
+__device__ __forceinline__ int xcd_grouped(int i, int n) {
+  const int x = i & 7, q8 = n >> 3, r8 = n & 7;
+  return x * q8 + min(x, r8) + (i >> 3);   // a bijection of [0, n): XCD x takes a run of v
+}
 template <typename T, int D>
 __global__ __launch_bounds__(kMergeThreads) void attn_reduce_kernel(const AttnArgs a) {
   constexpr int CH = D / 4;                 // 16-byte chunks of a head's fp32 row: 32 or 16
   constexpr int PL = kMergeThreads / CH;    // partition lanes: 16 or 32
   __shared__ float sm_m[PL], sm_l[PL];
   __shared__ f32x4 sm_acc[PL][CH];
-  const int h = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+  const bool flat = gridDim.y == 1;
+  const int v = flat ? xcd_grouped((int)blockIdx.x, a.Hq * a.S) : 0;
+  const int h = flat ? v % a.Hq : (int)blockIdx.x, s = flat ? v / a.Hq : (int)blockIdx.y, tid = threadIdx.x;
   const int ctx = a.ctx[s];
   if (ctx < 1 || ctx > a.max_ctx || ctx <= a.P) return;
   const int np = min((ctx + a.P - 1) / a.P, a.max_parts);
@@ -1930,7 +1942,8 @@ static void launch_reduce(hipStream_t st, const AttnArgs &a) {
     const dim3 grid((unsigned)((a.Hq + kReduceHeads - 1) / kReduceHeads), (unsigned)a.S);
     hipLaunchKernelGGL((attn_reduce_short_kernel<T, D>), grid, dim3(kThreads), 0, st, a);
   } else {
-    const dim3 grid((unsigned)a.Hq, (unsigned)a.S);
+    const int64_t n = (int64_t)a.Hq * a.S;
+    const dim3 grid = n * kMergeThreads < (int64_t(1) << 32) ? dim3((unsigned)n) : dim3((unsigned)a.Hq, (unsigned)a.S);
     hipLaunchKernelGGL((attn_reduce_kernel<T, D>), grid, dim3(kMergeThreads), 0, st, a);
   }
 }
