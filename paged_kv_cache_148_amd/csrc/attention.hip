@@ -863,6 +863,15 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   static_assert(!FUSE || !HM, "the fused write is built for the row layout");
   static_assert(NB >= 2, "the ring holds the tile being computed and at least one ahead");
   constexpr int D = 128;
+  // How the workgroup takes its items from the queue.  With the shallow ring (items of more than
+  // 512 tokens, or unsplit) it takes the next item only when the current one ends: nothing is held
+  // while a slower workgroup could still start it, which shortens the launch's tail (mha7b:
+  // 219 -> 211.5 us, gqa70b: 276 -> 273 us, same box), at the price of the next item's table and
+  // q loads at each boundary.  With the deep ring (partitions of at most 512 tokens: many short
+  // items, where those boundaries would cost more than the tail saves) it takes item k + 2 while
+  // item k runs, so that the next item's table chunks, q and first tiles are in flight across
+  // the boundary.
+  constexpr bool kLate = NB < kTileDepthDeep;
   __shared__ TileSmem sm;
   __shared__ LptSmem sched_sm;
   extern __shared__ int sm_dyn[];
@@ -871,10 +880,11 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   const int c16 = lane & 15, grp = lane >> 4;
   int *sm_pref = sm_dyn, *sm_ctx = sm_dyn + a.S, *sm_order = sm_dyn + 2 * a.S;
 
-  // The workgroup's items: it_0 = blockIdx.x and it_1 = gridDim.x + blockIdx.x (the longest
-  // items, so a fixed split costs little balance, and the launch makes no queue fetch), then
-  // one index per queue fetch, counted from 2 * gridDim.x.  The fetch for it_{k+2} is made
-  // while it_k runs, so both the current and the next item are always known.
+  // The workgroup's items: it_0 = blockIdx.x (with the deep ring also it_1 = gridDim.x +
+  // blockIdx.x: the longest items, so a fixed split costs little balance, and the launch makes
+  // no queue fetch), then one index per queue fetch, counted from gridDim.x (kLate) or from
+  // 2 * gridDim.x.  kLate: the fetch for it_{k+1} is made as it_k ends.  Otherwise the fetch for
+  // it_{k+2} is made while it_k runs, so both the current and the next item are always known.
   // Wide items pay where the sequences' blocks lie far apart (a pool scattered over hundreds of
   // MB: address translation then bounds the stream); on a pool whose consecutive blocks lie close
   // together one-head items stream faster.  Each wave samples 64 pairs of consecutive table
@@ -916,7 +926,7 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   sched.items = sched.nwide + sched.total - sched.nwide * a.hpi;
   const int total = sched.items;
   int w = (int)blockIdx.x;
-  int wn = a.persistent ? (int)(gridDim.x + blockIdx.x) : total;
+  int wn = a.persistent && !kLate ? (int)(gridDim.x + blockIdx.x) : total;
   if (w < total) {
     MItem cur = item_at<NB, WIDE>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
     MItem nxt;
@@ -1350,21 +1360,29 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
     // the stream's first tiles
     u32x4 kbuf[NB][4], vbuf[NB][4];
     u32x2 vbuf2[NB][HM ? 8 : 1];   // head-major V pieces (unused on the row layout)
+    if constexpr (!kLate) {
 #pragma unroll
-    for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
+      for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
+    }
 
     for (int k = 0;; ++k) {
       mbuf = k & 1;
-      // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
-      // copies into the current item's registers at the end of this iteration, so those
-      // copies never wait on memory.
-      nxt = item_at<NB, WIDE>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
-      table_chunks<B, WIDE>(a, nxt, 0, lane, tb_next);
-      table_chunks<B, WIDE>(a, nxt, 1, lane, tb_next_ahead);
-      load_item_q(nxt, qnext);
-      load_item_new(nxt, kn_nxt, vn_nxt);
-      new_i_nxt = new_tile(nxt);
-      new_phys_nxt = -1;
+      if constexpr (kLate) {
+        // this item's first NB - 1 tiles (its table chunks and q were loaded when it was taken)
+#pragma unroll
+        for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
+      } else {
+        // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
+        // copies into the current item's registers at the end of this iteration, so those
+        // copies never wait on memory.
+        nxt = item_at<NB, WIDE>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
+        table_chunks<B, WIDE>(a, nxt, 0, lane, tb_next);
+        table_chunks<B, WIDE>(a, nxt, 1, lane, tb_next_ahead);
+        load_item_q(nxt, qnext);
+        load_item_new(nxt, kn_nxt, vn_nxt);
+        new_i_nxt = new_tile(nxt);
+        new_phys_nxt = -1;
+      }
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
       // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
       // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
@@ -1385,17 +1403,18 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
         body(0);
         for (x = NB; x < cur.n_pad - NB; x += NB) body(x);
       }
-      // Take it_{k+2} from the queue now, NB tiles before this item ends (its index is first
-      // read at the merge below).  Taking it later than at the item's start keeps a slow
-      // workgroup from claiming a long item early that a faster one would finish sooner.
-      const bool fetch = a.persistent && tid == 0 && wn < total;
+      // Take the next item (kLate: it_{k+1}; else it_{k+2}) from the queue now, NB tiles
+      // before this item ends (its index is first read at the merge below).  Taking it later
+      // than at the item's start keeps a slow workgroup from claiming a long item early that a
+      // faster one would finish sooner.
+      const bool fetch = a.persistent && tid == 0 && (kLate || wn < total);
       unsigned fetched = 0u;
       if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (j == 0)
           issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1], vbuf2[NB - 1]);
-        else
+        else if constexpr (!kLate)
           issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1], vbuf2[j - 1]);
         __builtin_amdgcn_sched_barrier(0);
         if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
@@ -1415,12 +1434,27 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
         store_state(mb, wave);
       }
       if (lane == 0) sm.bad[mb][wave] = bad_cur;
-      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)(2 * gridDim.x + fetched) : total;
+      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)((kLate ? 1 : 2) * gridDim.x + fetched) : total;
       __syncthreads();
       if (cur.fill == 0)
         tile_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
       else if (cur.fill != 3)
         fill_group<uint16_t, D>(a, cur.s, cur.kvh0 * a.g, cur.width * a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
+      if constexpr (kLate) {
+        // the item just taken: its table chunks, q and new rows
+        w = a.persistent ? sm.nextw[k & 1] : total;
+        if (w >= total) break;
+        cur = item_at<NB, WIDE>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
+        table_chunks<B, WIDE>(a, cur, 0, lane, tb_cur);
+        table_chunks<B, WIDE>(a, cur, 1, lane, tb_ahead);
+        load_item_q(cur, qop);
+        load_item_new(cur, kn_cur, vn_cur);
+        new_i_cur = new_tile(cur);
+        new_phys_cur = -1;
+        bad_cur = 0;
+        reset_state();
+        continue;
+      }
       if (wn >= total) break;
 
       // advance the stream by one item
