@@ -35,8 +35,20 @@ import workloads  # noqa: E402
 
 METRIC = "paged decode attention: KV HBM GB/s (% of MI355X peak), µs/decode step"
 HBM_PEAK_GBS = 8000.0
-# split-context partition used per workload (0 = one work unit per (sequence, KV head))
-PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": 1024}
+# split-context partition used per workload (0 = one work unit per (sequence, KV head); None =
+# recomputed for each step by batch.balanced_partition: the fork workload's 16 sequences x 8 KV
+# heads are half as many items as there are compute units)
+PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": None}
+
+
+def partition_for(name: str, cfg, step, num_cus: int = 256) -> int:
+    """The partition size bench.py times for workload `name` on this step's inputs."""
+    P = PARTITION[name]
+    if P is None:
+        from paged_kv_cache_148_amd import batch
+        P = batch.balanced_partition(cfg.num_seqs, cfg.num_kv_heads, int(step.max_context_len), cfg.block_size,
+                                     num_cus)
+    return P
 MAIN = "long_splitk"
 
 
@@ -138,6 +150,8 @@ def run_gpu(name: str, which: str, steps: int, warmup: int, partition: int, layo
             ids[i:i + window] = rng.permutation(ids[i:i + window])
         wl.free_order = [int(x) for x in ids[::-1]]
     step = batch.step_for(wl, which)
+    if partition is None:
+        partition = partition_for(name, cfg, step, torch.cuda.get_device_properties(0).multi_processor_count)
     bf16 = cfg.dtype == "bf16"
     dev = "cuda"
     q = batch.to_torch(wl.q, dev, bf16)
@@ -599,7 +613,8 @@ def main():
     # line of record's for ~10 s, the others once each; one thread as well on the two smallest)
     cpu_runs = {}
     if not args.no_cpu:
-        cpu_runs[args.workload] = cpu_baseline(wl, which, main_part, budget_s=10.0, gpu_results=res.pop("_results", None))
+        cpu_runs[args.workload] = cpu_baseline(wl, which, res["partition_size"], budget_s=10.0,
+                                               gpu_results=res.pop("_results", None))
         _say_cpu(args.workload, cpu_runs[args.workload])
     del wl, step
     others = {}
@@ -615,10 +630,11 @@ def main():
                 others[key] = r
                 _say_step(key, r)
                 if not args.no_cpu:
-                    cpu_runs[key] = cpu_baseline(wl_o, w, PARTITION[name], budget_s=0.0, gpu_results=r.pop("_results", None))
+                    cpu_runs[key] = cpu_baseline(wl_o, w, r["partition_size"], budget_s=0.0,
+                                                 gpu_results=r.pop("_results", None))
                     _say_cpu(key, cpu_runs[key])
                     if name in SINGLE_THREAD:
-                        single[key] = cpu_baseline(wl_o, w, PARTITION[name], budget_s=0.0, threads=1)
+                        single[key] = cpu_baseline(wl_o, w, r["partition_size"], budget_s=0.0, threads=1)
                         _say_cpu(key + " (1 thread)", single[key])
                 del wl_o, step_o
 
@@ -656,7 +672,7 @@ def main():
         "data": "synthetic (seeded N(0,1) q/K/V, seeded shuffled block pool)",
         "config": {"workload": f"{args.workload}: {cfg.description}", "num_seqs": cfg.num_seqs,
                    "num_heads": cfg.num_heads, "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
-                   "block_size": res["block_size"], "partition_size": main_part, "sum_ctx": res["sum_ctx"],
+                   "block_size": res["block_size"], "partition_size": res["partition_size"], "sum_ctx": res["sum_ctx"],
                    "max_ctx": res["max_ctx"], "parallelism": "single GPU"},
         "us_per_step": round(res["us_per_step"], 2),
         "step_us_events": {k: (round(v, 2) if isinstance(v, float) else v) for k, v in res["step_us_events"].items()},

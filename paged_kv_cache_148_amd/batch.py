@@ -99,6 +99,21 @@ def steady_fork_step(prompt_tokens: int, generated, num_blocks: int, block_size:
     return _finish(bm, seqs, ctx, slots, [])
 
 
+def balanced_partition(num_seqs: int, num_kv_heads: int, max_context_len: int, block_size: int,
+                       num_cus: int) -> int:
+    """A partition size for a batch with too few (sequence, KV head) work items to give every
+    compute unit one: the fewest equal pieces per sequence whose items cover every unit once,
+    rounded up to whole blocks (16 sequences x 8 KV heads on 256 units: two pieces).  0 (unsplit)
+    when the unsplit batch already covers them or a piece would be the whole context."""
+    units = num_seqs * num_kv_heads
+    if units <= 0 or units >= num_cus or max_context_len <= block_size:
+        return 0
+    parts = -(-num_cus // units)
+    p = -(-max_context_len // parts)
+    p = -(-p // block_size) * block_size
+    return p if p < max_context_len else 0
+
+
 # ---------------------------------------------------------------------------
 # upload
 # ---------------------------------------------------------------------------

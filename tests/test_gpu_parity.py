@@ -549,6 +549,7 @@ def test_split_matches_unsplit_within_tolerance():
 # ---------------------------------------------------------------------------
 
 from bench import PARTITION as BENCH_PARTITION  # noqa: E402  (the partitions bench.py times)
+from bench import partition_for as bench_partition  # noqa: E402
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "mha7b", "gqa70b", "long_splitk", "fork_cow"])
@@ -556,10 +557,10 @@ def test_full_size_parity(name):
     # the whole [S, Hq, D] output of each configuration at its full size against the fp64 oracle,
     # and both pools after the step's copies and writes bit for bit
     wl = _wl(name)
-    P = BENCH_PARTITION[name]
     whiches = ["fork", "steady"] if name == "fork_cow" else ["steady"]
     for which in whiches:
         step = pbatch.step_for(wl, which)
+        P = bench_partition(name, wl.cfg, step)
         _say("full", name, which, "S", wl.cfg.num_seqs, "P", P, "pool", wl.k_cache.shape)
         d = H.upload(wl, step)
         H.gpu_step(wl, step, d, P)
