@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0
 # split-context partition used per workload (0 = one work unit per (sequence, KV head); None =
 # recomputed for each step by batch.balanced_partition: the fork workload's 16 sequences x 8 KV
 # heads are half as many items as there are compute units)
-PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 2048, "long_splitk": 512, "fork_cow": None}
+PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 4096, "long_splitk": 512, "fork_cow": None}
 
 
 def partition_for(name: str, cfg, step, num_cus: int = 256) -> int:
@@ -88,15 +88,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, per_launch_alg: int):
+def measured_traffic(workload: str, partition, layout: str = "scattered"):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel sources; else None."""
+    taken on the current kernel sources at this partition size (on the default shuffled pool);
+    else None."""
     path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.json")
-    if not os.path.exists(path):
+    if layout != "scattered" or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or rec.get("partition_size") != partition:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -329,7 +330,7 @@ def roofline(name: str, res: dict, rd: dict | None) -> dict | None:
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(res["attention_alg_gbs"] / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(name, nb),
+        "traffic": measured_traffic(name, res.get("partition_size"), res.get("layout", "scattered")),
         "algorithmic_bytes_per_launch": nb,
         "launch_us_mean": round(res["attention_us_mean"], 2),
         "timing": f"HIP events around back-to-back attention calls on the launch stream",
