@@ -62,11 +62,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 // rounded up to a multiple of NB with empty tiles, whose slots carry no bytes at the item's
 // end; one tile ahead per wave already keeps the memory system saturated and wastes the
 // fewest slots.  The deep ring hides an item's merge and partial-state stores behind more
-// loads in flight, which pays when items are short partitions (at most 512 tokens: 8 tiles
-// per wave), whose lengths are also whole multiples of the ring.
+// loads in flight, which pays when items are very short partitions (at most 256 tokens: 4 tiles
+// per wave), whose lengths are also whole multiples of the ring.  At 512 tokens the shallow ring,
+// with its items taken just in time (attn_tile_kernel), is the faster: long contexts 548.4 ->
+// 540.5 us, gqa70b split at 512 305.5 -> 304.3 us, same box; at 256 the deep ring stays ahead on
+// the GQA shapes (gqa70b 538.0 against 543.1 us, the fork workload 35.6 against 37.8 us).
 constexpr int kTileDepthShallow = 2;
 constexpr int kTileDepthDeep = 4;
-constexpr int64_t kDeepRingMaxPartition = 512;
+constexpr int64_t kDeepRingMaxPartition = 256;
 constexpr int kMaxReduceParts = 8192;    // partials per (sequence, head) a call may have
 constexpr int kMaxSchedSeqs = 4096;     // sequences whose schedule fits in LDS (up to 3 x 16 KiB)
 constexpr int kClasses = 16;            // length classes of the longest-first schedule
@@ -864,10 +867,10 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   static_assert(NB >= 2, "the ring holds the tile being computed and at least one ahead");
   constexpr int D = 128;
   // How the workgroup takes its items from the queue.  With the shallow ring (items of more than
-  // 512 tokens, or unsplit) it takes the next item only when the current one ends: nothing is held
+  // 256 tokens, or unsplit) it takes the next item only when the current one ends: nothing is held
   // while a slower workgroup could still start it, which shortens the launch's tail (mha7b:
   // 219 -> 211.5 us, gqa70b: 276 -> 273 us, same box), at the price of the next item's table and
-  // q loads at each boundary.  With the deep ring (partitions of at most 512 tokens: many short
+  // q loads at each boundary.  With the deep ring (partitions of at most 256 tokens: many short
   // items, where those boundaries would cost more than the tail saves) it takes item k + 2 while
   // item k runs, so that the next item's table chunks, q and first tiles are in flight across
   // the boundary.
@@ -1920,7 +1923,7 @@ static Pass1Fn tile_hm_fn(int B) {
   }
 }
 
-// deep: the MFMA tiles' deep load ring (split into partitions of at most 512 tokens).  One
+// deep: the MFMA tiles' deep load ring (split into partitions of at most 256 tokens).  One
 // query head per KV head keeps the shallow ring: its merge and stores are a single head's.
 // fuse: the fused write of the new tokens (row layout, tile paths, shallow ring: the new rows
 // take the registers the deep ring would need).
