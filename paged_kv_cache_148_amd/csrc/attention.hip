@@ -77,7 +77,7 @@ constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the
 // Wide work items (tile paths, row layout): at least kWideMinItems of them per workgroup, and the
 // queue's last kWideReserve one-head items per workgroup stay one head wide (the finer tail).
 constexpr int kWideMinItems = 4;
-constexpr int kWideReserve = 4;
+constexpr int kWideReserve = 2;   // with items taken just in time 2 beat 0, 4 and 8 (mha7b, gqa70b)
 // ... and only where the sampled consecutive blocks of the sequences lie this far apart (in one
 // pool): on pools shuffled within windows of 32 MB one-head items were faster, within 256 MB and
 // beyond wide ones (long contexts, 512-token partitions).
