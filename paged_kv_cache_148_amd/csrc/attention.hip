@@ -1387,9 +1387,10 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
         new_phys_nxt = -1;
       }
       // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
-      // of NB, so the last NB - 1 steps issue the next item's tiles 0 .. NB-2 into buffers
-      // 0 .. NB-2.  That last body is a separate copy, so the wait on the next item's table
-      // entries sits only there.
+      // of NB, so (two-ahead claims) the last NB - 1 steps issue the next item's tiles
+      // 0 .. NB-2 into buffers 0 .. NB-2; with kLate they issue nothing, and the next item's
+      // first tiles go out at the top of its own iteration.  That last body is a separate copy,
+      // so the wait on the next item's table entries sits only there.
       // The first body is a copy of its own too: its waits count the loads and stores
       // issued since this item's first tiles (the merge, the next item's table and q), so
       // it does not wait for more tiles than the one it computes.
