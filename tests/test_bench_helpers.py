@@ -150,3 +150,18 @@ def test_bench_partition_for_the_fork_workload():
     P = bench.partition_for("fork_cow", wl.cfg, steady)
     assert P % 16 == 0 and 2 * P >= steady.max_context_len > P    # two pieces per sequence
     assert bench.partition_for("long_splitk", wl.cfg, steady) == 512
+
+
+def test_traffic_record_applies_only_where_it_was_taken(tmp_path, monkeypatch):
+    import json
+    (tmp_path / "profiles").mkdir()
+    rec = {"kernel_source_hash": bench.kernel_source_hash(), "partition_size": 512, "hbm_bytes_per_launch": 123}
+    (tmp_path / "profiles" / "attention_traffic_long_splitk.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("long_splitk", 512) == 123
+    assert bench.measured_traffic("long_splitk", 1024) is None            # another partition size
+    assert bench.measured_traffic("long_splitk", 512, "contiguous") is None  # another pool
+    assert bench.measured_traffic("mha7b", 0) is None                      # no record
+    rec["kernel_source_hash"] = "0" * 16                                   # other kernel sources
+    (tmp_path / "profiles" / "attention_traffic_long_splitk.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("long_splitk", 512) is None
