@@ -155,9 +155,11 @@ def test_bench_partition_for_the_fork_workload():
 def test_traffic_record_applies_only_where_it_was_taken(tmp_path, monkeypatch):
     import json
     (tmp_path / "profiles").mkdir()
-    rec = {"kernel_source_hash": bench.kernel_source_hash(), "partition_size": 512, "hbm_bytes_per_launch": 123}
+    h = bench.kernel_source_hash()
+    rec = {"kernel_source_hash": h, "partition_size": 512, "hbm_bytes_per_launch": 123}
     (tmp_path / "profiles" / "attention_traffic_long_splitk.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
     assert bench.measured_traffic("long_splitk", 512) == 123
     assert bench.measured_traffic("long_splitk", 1024) is None            # another partition size
     assert bench.measured_traffic("long_splitk", 512, "contiguous") is None  # another pool
