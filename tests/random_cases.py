@@ -6,7 +6,7 @@ for blocks of at most 32 slots and up to 8 query heads per KV head), and the GPU
 that the library selects the same path."""
 import numpy as np
 
-N_CASES = 40
+N_CASES = 80
 MAX_WORKSPACE = 256 << 20
 
 
