@@ -772,45 +772,60 @@ __device__ __forceinline__ MItem item_at(const AttnArgs &a, int w, const LptSche
 
 // Merge of the four phase states of each head of an item, then its output (normalised, or a
 // partial state for the second pass).  Thread t covers row t / 16 of the item's query heads
-// (the KV heads' groups one after the other) and head dims 4l .. 4l + 3 and 64 + 4l .. +3
-// (l = t % 16): ten independent LDS reads and one wait.  Each store instruction then writes
-// whole 256-byte runs of a head's row (16 lanes, consecutive 16-byte pieces), so every line of
-// the write-through partial states is written at once: with each lane's 8 consecutive dims
-// instead, an instruction left every 32-byte sector half written and the memory side counted
-// twice the records' bytes.
+// (the KV heads' groups one after the other).  It reads head dims 8l .. 8l + 7 (l = t % 16) of
+// each wave's state: ten independent LDS reads, one wait, and no bank conflicts with the padded
+// row stride (whereas 4 dims per lane, 16 bytes apart, left every read 2-way conflicted).  The
+// merged values are then regrouped across the row's 16 lanes so that thread t holds dims
+// 4l .. 4l + 3 and 64 + 4l .. + 3: each store instruction then writes whole 256-byte runs of a
+// head's row (16 lanes, consecutive 16-byte pieces), so every line of the write-through partial
+// states is written at once (with each lane's 8 consecutive dims an instruction left every
+// 32-byte sector half written, and the memory side counted twice the records' bytes).
 __device__ __forceinline__ void tile_finish(const AttnArgs &a, const MItem &it, const float (*sm_m)[kWaves],
                                             const float (*sm_l)[kWaves], const float (*sm_o)[16][kTileOS],
                                             const int *sm_bad) {
   constexpr int D = 128;
-  const int t = threadIdx.x, j = t >> 4, d0 = (t & 15) * 4, d1 = 64 + d0;
+  const int t = threadIdx.x, lane = t & 63, j = t >> 4, l = t & 15, e0 = 8 * l;
+  const int d0 = 4 * l, d1 = 64 + d0;   // the dims this thread stores
   // row j: query head j of the item's heads (head jj of KV head kvh0 + u)
   const int u = j / a.g, jj = j - u * a.g;
   const bool act = u < it.width;   // rows past the item's heads: their LDS rows are read, not used
   const f32x4 m4 = *reinterpret_cast<const f32x4 *>(sm_m[j]);
   const f32x4 l4 = *reinterpret_cast<const f32x4 *>(sm_l[j]);
-  f32x4 olo[kWaves], ohi[kWaves];
+  f32x4 oa[kWaves], ob[kWaves];
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    olo[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d0]);
-    ohi[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][d1]);
+    oa[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][e0]);
+    ob[w] = *reinterpret_cast<const f32x4 *>(&sm_o[w][j][e0 + 4]);
   }
   const bool bad = sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3];
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m4[w]);
   float L = 0.f;
-  f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};   // dims 8l .. 8l + 3, 8l + 4 .. 8l + 7
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const float wt = merge_weight(m4[w], M);
     L += wt * l4[w];
-    lo += wt * olo[w];
-    hi += wt * ohi[w];
+    va += wt * oa[w];
+    vb += wt * ob[w];
   }
   if (bad) {
     M = 0.f;
     L = __builtin_nanf("");
-    lo = hi = (f32x4){L, L, L, L};
+    va = vb = (f32x4){L, L, L, L};
+  }
+  // dims 4l .. 4l + 3 are lane l / 2's va (l even) or vb (l odd); dims 64 + 4l .. + 3 are lane
+  // 8 + l / 2's, the same way (lanes of this row: the 16 of this thread's group in the wave)
+  const int src_lo = (lane & 48) | (l >> 1), src_hi = (lane & 48) | (8 + (l >> 1));
+  const bool odd = l & 1;
+  f32x4 lo, hi;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float x0 = __shfl(va[e], src_lo), x1 = __shfl(vb[e], src_lo);
+    const float y0 = __shfl(va[e], src_hi), y1 = __shfl(vb[e], src_hi);
+    lo[e] = odd ? x1 : x0;
+    hi[e] = odd ? y1 : y0;
   }
   // the item's first head h0: every store below goes through one wave-uniform descriptor
   // based there, with a 32-bit per-lane offset (the item's KV heads are adjacent)
