@@ -48,6 +48,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "pkv.h"
 #include "pkv_device.h"
@@ -621,14 +622,15 @@ template <int NB>
 __device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int kvh, int ctx, int wave,
                                            int width) {
   MItem it;
-  const int wph = kWaves / width;
+  const int lw = __builtin_ctz((unsigned)width);   // width 1, 2 or 4: shifts, not divisions
+  const int wph = kWaves >> lw;
   it.s = s;
   it.p = p;
   it.kvh0 = kvh;
-  it.u = wave / wph;
+  it.u = (int)((unsigned)(wave * width) / kWaves);
   it.kvh = kvh + it.u;
   it.width = width;
-  it.ph0 = wave % wph;
+  it.ph0 = wave & (wph - 1);
   it.pst = wph;
   it.tile_lo = (p * a.P) >> 4;
   it.t0 = p * a.P;
@@ -665,9 +667,11 @@ __device__ __forceinline__ MItem make_item(const AttnArgs &a, int s, int p, int 
 template <bool WIDE>
 __device__ __forceinline__ int tile_of(const MItem &it, int i) {
   if constexpr (!WIDE) return it.tile_lo + it.ph0 + kWaves * i;
-  const int k = (i >= it.b1) + (i >= it.b2) + (i >= it.b3);
-  const int start = k == 0 ? 0 : k == 1 ? it.b1 : k == 2 ? it.b2 : it.b3;
-  return it.tile_lo + it.ph0 + k * it.pst + kWaves * (i - start);
+  // b1 <= b2 <= b3: the phase of index i began at the largest of them not above i (selects and
+  // maxima, not a branch per phase)
+  const bool k1 = i >= it.b1, k2 = i >= it.b2, k3 = i >= it.b3;
+  const int start = max(max(k1 ? it.b1 : 0, k2 ? it.b2 : 0), k3 ? it.b3 : 0);
+  return it.tile_lo + it.ph0 + ((int)k1 + (int)k2 + (int)k3) * it.pst + kWaves * (i - start);
 }
 
 // Blocks that one 16-token tile spans: 16 / B for blocks of 4 or 8 slots, else 1.
@@ -943,561 +947,573 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   sched.nwide = go_wide ? max(0, sched.total - a.reserve) / a.hpi : 0;
   sched.items = sched.nwide + sched.total - sched.nwide * a.hpi;
   const int total = sched.items;
-  int w = (int)blockIdx.x;
-  int wn = a.persistent && !kLate ? (int)(gridDim.x + blockIdx.x) : total;
-  if (w < total) {
-    MItem cur = item_at<NB, WIDE>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
-    MItem nxt;
+  // The item loop, built twice in the wide-item kernel: a launch that hands out no wide items (a
+  // pool whose blocks lie close together) runs the one-head loop, whose phase bookkeeping is
+  // shorter, and so streams as the one-head kernel does; the outputs are the same bits either way.
+  auto run_items = [&](auto wide_c) {
+    constexpr bool WI = decltype(wide_c)::value;
+    int w = (int)blockIdx.x;
+    int wn = a.persistent && !kLate ? (int)(gridDim.x + blockIdx.x) : total;
+    if (w < total) {
+      MItem cur = item_at<NB, WI>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
+      MItem nxt;
 
-    // Token of a tile row.  Load instruction r gives lane group grp the tile token
-    //   tok(grp, r) = blk * B + (4 / BPT) * grp + r % (4 / BPT),   blk = r / (4 / BPT),
-    // BPT = blocks per tile: with blocks of 16 or more it is 4grp + r; with smaller blocks
-    // every instruction stays inside one block (blk), so one buffer descriptor serves it.
-    // The MFMA row of that token is 4grp + r throughout (K staging, scores, P, V alike), so
-    // the only effect is the order of the tile's tokens in the P.V sum.
-    constexpr int BPT = tile_blocks<B>();
-    constexpr int RPI = 4 / BPT;   // consecutive load instructions per block
-    const uint32_t tsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive slots
-    const uint32_t blk_bytes = (BPT == 1 ? 16 : B) * tsb;   // range of one descriptor
-    const char *kpool = reinterpret_cast<const char *>(a.k);
-    const char *vpool = reinterpret_cast<const char *>(a.v);
-    const uint32_t row_voff = RPI * grp * tsb + 16 * c16;   // whole 256-byte rows, bytes 16 c16
-    u32x4 *kst = sm.kst[wave];
+      // Token of a tile row.  Load instruction r gives lane group grp the tile token
+      //   tok(grp, r) = blk * B + (4 / BPT) * grp + r % (4 / BPT),   blk = r / (4 / BPT),
+      // BPT = blocks per tile: with blocks of 16 or more it is 4grp + r; with smaller blocks
+      // every instruction stays inside one block (blk), so one buffer descriptor serves it.
+      // The MFMA row of that token is 4grp + r throughout (K staging, scores, P, V alike), so
+      // the only effect is the order of the tile's tokens in the P.V sum.
+      constexpr int BPT = tile_blocks<B>();
+      constexpr int RPI = 4 / BPT;   // consecutive load instructions per block
+      const uint32_t tsb = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive slots
+      const uint32_t blk_bytes = (BPT == 1 ? 16 : B) * tsb;   // range of one descriptor
+      const char *kpool = reinterpret_cast<const char *>(a.k);
+      const char *vpool = reinterpret_cast<const char *>(a.v);
+      const uint32_t row_voff = RPI * grp * tsb + 16 * c16;   // whole 256-byte rows, bytes 16 c16
+      u32x4 *kst = sm.kst[wave];
 
-    // registers of the stream: table chunks (current item: the chunk being issued and the
-    // one after it; next item: its first two; one register per block of a tile), q operands,
-    // validity flags
-    int tb_cur[BPT], tb_ahead[BPT], tb_next[BPT], tb_next_ahead[BPT];
-    table_chunks<B, WIDE>(a, cur, 0, lane, tb_cur);
-    table_chunks<B, WIDE>(a, cur, 1, lane, tb_ahead);
-    // q operands: MF, head c16 of the group in the B layout; !MF on the head-major layout, the
-    // item's head at the K chunks lane group grp holds (dims 32c + 8grp); !MF on the row
-    // layout, dims 8 c16 .. + 7
-    auto load_item_q = [&](const MItem &it, u32x4 *qd) {
-      if constexpr (MF) load_q(a, it, c16, grp, qd);
-      else if constexpr (HM) load_q(a, it, 0, grp, qd);
-      else load_q_row(a, it, c16, qd);
-    };
-    u32x4 qop[4], qnext[4];
-    load_item_q(cur, qop);
-    int bad_cur = 0, bad_next = 0;
+      // registers of the stream: table chunks (current item: the chunk being issued and the
+      // one after it; next item: its first two; one register per block of a tile), q operands,
+      // validity flags
+      int tb_cur[BPT], tb_ahead[BPT], tb_next[BPT], tb_next_ahead[BPT];
+      table_chunks<B, WI>(a, cur, 0, lane, tb_cur);
+      table_chunks<B, WI>(a, cur, 1, lane, tb_ahead);
+      // q operands: MF, head c16 of the group in the B layout; !MF on the head-major layout, the
+      // item's head at the K chunks lane group grp holds (dims 32c + 8grp); !MF on the row
+      // layout, dims 8 c16 .. + 7
+      auto load_item_q = [&](const MItem &it, u32x4 *qd) {
+        if constexpr (MF) load_q(a, it, c16, grp, qd);
+        else if constexpr (HM) load_q(a, it, 0, grp, qd);
+        else load_q_row(a, it, c16, qd);
+      };
+      u32x4 qop[4], qnext[4];
+      load_item_q(cur, qop);
+      int bad_cur = 0, bad_next = 0;
 
-    // The fused write.  The item whose partition holds a sequence's new token (position
-    // ctx - 1) stores that token's K and V rows of its KV head, from k_new and v_new, into the
-    // token's slot, and the wave whose tile holds the token puts the same bytes in place of the
-    // (stale) row it loaded before using it: the row is used from registers, so nothing waits
-    // on the store.  Lane (c16, grp) holds bytes 16 c16 .. 16 c16 + 15 of its rows, so each lane
-    // loads that piece of the new rows, with the item's q.
-    u32x4 kn_cur = {0u, 0u, 0u, 0u}, vn_cur = kn_cur, kn_nxt = kn_cur, vn_nxt = kn_cur;
-    // the item's partition holds the context's last token
-    auto is_last = [&](const MItem &it) -> bool {
-      const int c = a.persistent ? sm_ctx[it.s] : a.ctx[it.s];
-      return it.fill == 0 && it.t1 == __builtin_amdgcn_readfirstlane(c);
-    };
-    auto load_item_new = [&](const MItem &it, u32x4 &kn, u32x4 &vn) {
-      if constexpr (FUSE) {
-        const uint32_t range = is_last(it) ? (uint32_t)(D * 2) : 0u;
-        const size_t row = ((size_t)it.s * a.Hkv + it.kvh) * D;
-        kn = __builtin_amdgcn_raw_buffer_load_b128(
-            buf_rsrc(reinterpret_cast<const uint16_t *>(a.k_new) + row, range), 16 * c16, 0, 0);
-        vn = __builtin_amdgcn_raw_buffer_load_b128(
-            buf_rsrc(reinterpret_cast<const uint16_t *>(a.v_new) + row, range), 16 * c16, 0, 0);
-      }
-    };
-    // this wave's index of the tile holding the item's new token, or -1
-    auto new_tile = [&](const MItem &it) -> int {
-      if (!FUSE || !is_last(it)) return -1;
-      const int rel = ((it.t1 - 1) >> 4) - it.tile_lo;
-      const int q = rel & (kWaves - 1), k = q / it.pst;
-      if (q - k * it.pst != it.ph0) return -1;
-      return (k == 0 ? 0 : k == 1 ? it.b1 : k == 2 ? it.b2 : it.b3) + (rel >> 2);
-    };
-    // the table entry of the new token's block is taken when its tile is issued (-1: outside
-    // the pool, so the row is not stored); hn: that block among the tile's
-#define PKV_NEW_BLOCK(IT, RAW, DST)                                             \
-  do {                                                                          \
-    const int hn_ = BPT == 1 ? 0 : (((IT).t1 - 1) & 15) / B;                    \
-    int e_ = (RAW)[0];                                                          \
-    _Pragma("unroll") for (int h_ = 1; h_ < BPT; ++h_) if (h_ == hn_) e_ = (RAW)[h_]; \
-    (DST) = (unsigned)e_ < (unsigned)a.N ? e_ : -1;                             \
-  } while (0)
-    load_item_new(cur, kn_cur, vn_cur);
-    int new_i_cur = new_tile(cur), new_i_nxt = -1, new_phys_cur = -1, new_phys_nxt = -1;
-
-    // Loads of tile i of an item (zero-range descriptors past its live tiles).
-    auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
-      const bool live = i < it.n_my;
-      const int tok0 = tile_of<WIDE>(it, i) << 4;
-      if constexpr (HM) {
-        constexpr uint32_t hb_bytes = D * B * 2;   // one (block, KV head) of K or of V
-        const size_t off = ((size_t)phys[0] * a.Hkv + it.kvh) * hb_bytes;
-        const uint32_t range = live ? hb_bytes : 0u;
-        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kpool + off, range);
-        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vpool + off, range);
-        const int t0b = tok0 % B;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          kd[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, (grp * B + c16) * 16, (4 * c * B + t0b) * 16, kNontemporal);
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          vd2[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (c16 * B + 4 * grp) * 2, (16 * j * B + t0b) * 2, kNontemporal);
-        return;
-      }
-      __amdgpu_buffer_rsrc_t rk[BPT], rv[BPT];
-#pragma unroll
-      for (int h = 0; h < BPT; ++h) {
-        // a block of the tile that lies wholly past the range (its table entry is padding) or
-        // a tile past the item's live ones: zero-range descriptor, no memory access
-        const uint32_t range = live && tok0 + h * B < it.t1 ? blk_bytes : 0u;
-        // the tile's rows in block h (B >= 16: the 16 rows from offset tok0 % B)
-        const size_t off = ((size_t)phys[h] * B + (BPT == 1 ? tok0 % B : 0)) * tsb + (size_t)it.kvh * D * 2;
-        rk[h] = buf_rsrc(kpool + off, range);
-        rv[h] = buf_rsrc(vpool + off, range);
-      }
-      // K and V alike: instruction r reads whole 256-byte rows (16 lanes per row), streamed
-      // past the caches (non-temporal).
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
-    };
-    // tile i of the current item
-    auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
-      const bool live = i < cur.n_my;
-      if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
-#pragma unroll
-        for (int h = 0; h < BPT; ++h) tb_cur[h] = tb_ahead[h];
-        table_chunks<B, WIDE>(a, cur, (i >> 6) + 1, lane, tb_ahead);
-      }
-      const int tok0 = tile_of<WIDE>(cur, i) << 4;
-      int phys[BPT];
-      if constexpr (FUSE) {
-#pragma unroll
-        for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
-        if (i == new_i_cur) PKV_NEW_BLOCK(cur, phys, new_phys_cur);
-      }
-#pragma unroll
-      for (int h = 0; h < BPT; ++h) {
-        if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
-        if ((unsigned)phys[h] >= (unsigned)a.N) {
-          if (live && tok0 + h * B < cur.t1) bad_cur = 1;   // an entry the range reads
-          phys[h] = 0;
+      // The fused write.  The item whose partition holds a sequence's new token (position
+      // ctx - 1) stores that token's K and V rows of its KV head, from k_new and v_new, into the
+      // token's slot, and the wave whose tile holds the token puts the same bytes in place of the
+      // (stale) row it loaded before using it: the row is used from registers, so nothing waits
+      // on the store.  Lane (c16, grp) holds bytes 16 c16 .. 16 c16 + 15 of its rows, so each lane
+      // loads that piece of the new rows, with the item's q.
+      u32x4 kn_cur = {0u, 0u, 0u, 0u}, vn_cur = kn_cur, kn_nxt = kn_cur, vn_nxt = kn_cur;
+      // the item's partition holds the context's last token
+      auto is_last = [&](const MItem &it) -> bool {
+        const int c = a.persistent ? sm_ctx[it.s] : a.ctx[it.s];
+        return it.fill == 0 && it.t1 == __builtin_amdgcn_readfirstlane(c);
+      };
+      auto load_item_new = [&](const MItem &it, u32x4 &kn, u32x4 &vn) {
+        if constexpr (FUSE) {
+          const uint32_t range = is_last(it) ? (uint32_t)(D * 2) : 0u;
+          const size_t row = ((size_t)it.s * a.Hkv + it.kvh) * D;
+          kn = __builtin_amdgcn_raw_buffer_load_b128(
+              buf_rsrc(reinterpret_cast<const uint16_t *>(a.k_new) + row, range), 16 * c16, 0, 0);
+          vn = __builtin_amdgcn_raw_buffer_load_b128(
+              buf_rsrc(reinterpret_cast<const uint16_t *>(a.v_new) + row, range), 16 * c16, 0, 0);
         }
-      }
-      load_tile(cur, i, phys, kd, vd, vd2);
-    };
-    // tile i (< NB - 1) of the next item
-    auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
-      const int tok0 = tile_of<WIDE>(nxt, i) << 4;
-      int phys[BPT];
-      if constexpr (FUSE) {
+      };
+      // this wave's index of the tile holding the item's new token, or -1
+      auto new_tile = [&](const MItem &it) -> int {
+        if (!FUSE || !is_last(it)) return -1;
+        const int rel = ((it.t1 - 1) >> 4) - it.tile_lo;
+        const int q = rel & (kWaves - 1), k = q / it.pst;
+        if (q - k * it.pst != it.ph0) return -1;
+        return (k == 0 ? 0 : k == 1 ? it.b1 : k == 2 ? it.b2 : it.b3) + (rel >> 2);
+      };
+      // the table entry of the new token's block is taken when its tile is issued (-1: outside
+      // the pool, so the row is not stored); hn: that block among the tile's
+#define PKV_NEW_BLOCK(IT, RAW, DST)                                             \
+    do {                                                                          \
+      const int hn_ = BPT == 1 ? 0 : (((IT).t1 - 1) & 15) / B;                    \
+      int e_ = (RAW)[0];                                                          \
+      _Pragma("unroll") for (int h_ = 1; h_ < BPT; ++h_) if (h_ == hn_) e_ = (RAW)[h_]; \
+      (DST) = (unsigned)e_ < (unsigned)a.N ? e_ : -1;                             \
+    } while (0)
+      load_item_new(cur, kn_cur, vn_cur);
+      int new_i_cur = new_tile(cur), new_i_nxt = -1, new_phys_cur = -1, new_phys_nxt = -1;
+
+      // Loads of tile i of an item (zero-range descriptors past its live tiles).
+      auto load_tile = [&](const MItem &it, int i, const int *phys, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
+        const bool live = i < it.n_my;
+        const int tok0 = tile_of<WI>(it, i) << 4;
+        if constexpr (HM) {
+          constexpr uint32_t hb_bytes = D * B * 2;   // one (block, KV head) of K or of V
+          const size_t off = ((size_t)phys[0] * a.Hkv + it.kvh) * hb_bytes;
+          const uint32_t range = live ? hb_bytes : 0u;
+          const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kpool + off, range);
+          const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vpool + off, range);
+          const int t0b = tok0 % B;
 #pragma unroll
-        for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
-        if (i == new_i_nxt) PKV_NEW_BLOCK(nxt, phys, new_phys_nxt);
-      }
+          for (int c = 0; c < 4; ++c)
+            kd[c] = __builtin_amdgcn_raw_buffer_load_b128(rk, (grp * B + c16) * 16, (4 * c * B + t0b) * 16, kNontemporal);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            vd2[j] = __builtin_amdgcn_raw_buffer_load_b64(rv, (c16 * B + 4 * grp) * 2, (16 * j * B + t0b) * 2, kNontemporal);
+          return;
+        }
+        __amdgpu_buffer_rsrc_t rk[BPT], rv[BPT];
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+          // a block of the tile that lies wholly past the range (its table entry is padding) or
+          // a tile past the item's live ones: zero-range descriptor, no memory access
+          const uint32_t range = live && tok0 + h * B < it.t1 ? blk_bytes : 0u;
+          // the tile's rows in block h (B >= 16: the 16 rows from offset tok0 % B)
+          const size_t off = ((size_t)phys[h] * B + (BPT == 1 ? tok0 % B : 0)) * tsb + (size_t)it.kvh * D * 2;
+          rk[h] = buf_rsrc(kpool + off, range);
+          rv[h] = buf_rsrc(vpool + off, range);
+        }
+        // K and V alike: instruction r reads whole 256-byte rows (16 lanes per row), streamed
+        // past the caches (non-temporal).
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          kd[r] = __builtin_amdgcn_raw_buffer_load_b128(rk[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          vd[r] = __builtin_amdgcn_raw_buffer_load_b128(rv[r / RPI], row_voff, (r % RPI) * tsb, kNontemporal);
+      };
+      // tile i of the current item
+      auto issue_cur = [&](int i, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
+        const bool live = i < cur.n_my;
+        if (live && i > 0 && (i & 63) == 0) {   // into the next chunk of this item's table entries
+#pragma unroll
+          for (int h = 0; h < BPT; ++h) tb_cur[h] = tb_ahead[h];
+          table_chunks<B, WI>(a, cur, (i >> 6) + 1, lane, tb_ahead);
+        }
+        const int tok0 = tile_of<WI>(cur, i) << 4;
+        int phys[BPT];
+        if constexpr (FUSE) {
+#pragma unroll
+          for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
+          if (i == new_i_cur) PKV_NEW_BLOCK(cur, phys, new_phys_cur);
+        }
+#pragma unroll
+        for (int h = 0; h < BPT; ++h) {
+          if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_cur[h], i & 63);
+          if ((unsigned)phys[h] >= (unsigned)a.N) {
+            if (live && tok0 + h * B < cur.t1) bad_cur = 1;   // an entry the range reads
+            phys[h] = 0;
+          }
+        }
+        load_tile(cur, i, phys, kd, vd, vd2);
+      };
+      // tile i (< NB - 1) of the next item
+      auto issue_next = [&](int i, const int *tb_nx, u32x4 *kd, u32x4 *vd, u32x2 *vd2) {
+        const int tok0 = tile_of<WI>(nxt, i) << 4;
+        int phys[BPT];
+        if constexpr (FUSE) {
+#pragma unroll
+          for (int h = 0; h < BPT; ++h) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
+          if (i == new_i_nxt) PKV_NEW_BLOCK(nxt, phys, new_phys_nxt);
+        }
 #undef PKV_NEW_BLOCK
 #pragma unroll
-      for (int h = 0; h < BPT; ++h) {
-        if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
-        if ((unsigned)phys[h] >= (unsigned)a.N) {
-          if (i < nxt.n_my && tok0 + h * B < nxt.t1) bad_next = 1;
-          phys[h] = 0;
+        for (int h = 0; h < BPT; ++h) {
+          if constexpr (!FUSE) phys[h] = __builtin_amdgcn_readlane(tb_nx[h], i);
+          if ((unsigned)phys[h] >= (unsigned)a.N) {
+            if (i < nxt.n_my && tok0 + h * B < nxt.t1) bad_next = 1;
+            phys[h] = 0;
+          }
         }
-      }
-      load_tile(nxt, i, phys, kd, vd, vd2);
-    };
+        load_tile(nxt, i, phys, kd, vd, vd2);
+      };
 
-    // accumulators: MF, MFMA i's 16x16 tile; !MF, head dims 8 c16 + 4i + e of this lane group's
-    // tokens (e = 0..3), summed over the lane groups at the merge
-    constexpr int NACC = MF ? 8 : 2;
-    float m = kNegInf, lsum = 0.f;
-    f32x4 acc[NACC];
-#pragma unroll
-    for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    int mbuf = 0;   // the current item's merge buffer
-    auto reset_state = [&]() {
-      m = kNegInf;
-      lsum = 0.f;
+      // accumulators: MF, MFMA i's 16x16 tile; !MF, head dims 8 c16 + 4i + e of this lane group's
+      // tokens (e = 0..3), summed over the lane groups at the merge
+      constexpr int NACC = MF ? 8 : 2;
+      float m = kNegInf, lsum = 0.f;
+      f32x4 acc[NACC];
 #pragma unroll
       for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    };
-    // This wave's state of one phase into merge buffer mb, slot `slot`, rows of its KV head:
-    // (m, l) of each head and its unnormalised rows; the item's sum is spread over the lane
-    // groups except on the head-major VALU path.
-    auto store_state = [&](int mb, int slot) {
-      float lh = lsum;
-      if constexpr (MF || !HM) {
-        lh += __shfl_xor(lh, 16);
-        lh += __shfl_xor(lh, 32);
-      }
-      const int row = WIDE ? cur.u * a.g + c16 : c16;     // MF: head c16 of this wave's group
-      const bool own = !WIDE || c16 < a.g;                // (one-head items write all 16 rows)
-      const int urow = WIDE ? cur.u : 0;                  // !MF: the wave's one head
-      if constexpr (MF) {
-        if (grp == 0 && own) {
-          sm.m[mb][row][slot] = m;
-          sm.l[mb][row][slot] = lh;
+      int mbuf = 0;   // the current item's merge buffer
+      auto reset_state = [&]() {
+        m = kNegInf;
+        lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      };
+      // This wave's state of one phase into merge buffer mb, slot `slot`, rows of its KV head:
+      // (m, l) of each head and its unnormalised rows; the item's sum is spread over the lane
+      // groups except on the head-major VALU path.
+      auto store_state = [&](int mb, int slot) {
+        float lh = lsum;
+        if constexpr (MF || !HM) {
+          lh += __shfl_xor(lh, 16);
+          lh += __shfl_xor(lh, 32);
         }
-      } else if (lane == 0) {   // one head: m is the same in every lane
-        sm.m[mb][urow][slot] = m;
-        sm.l[mb][urow][slot] = lh;
-      }
-      if constexpr (!MF) {   // the lane groups' sums, then dims 8 c16 .. + 7 from lane group 0
-#pragma unroll
-        for (int i = 0; i < NACC; ++i) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float x = acc[i][e];
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            acc[i][e] = x;
+        const int row = WI ? cur.u * a.g + c16 : c16;     // MF: head c16 of this wave's group
+        const bool own = !WI || c16 < a.g;                // (one-head items write all 16 rows)
+        const int urow = WI ? cur.u : 0;                  // !MF: the wave's one head
+        if constexpr (MF) {
+          if (grp == 0 && own) {
+            sm.m[mb][row][slot] = m;
+            sm.l[mb][row][slot] = lh;
           }
+        } else if (lane == 0) {   // one head: m is the same in every lane
+          sm.m[mb][urow][slot] = m;
+          sm.l[mb][urow][slot] = lh;
         }
-        if (grp == 0) {
-          if constexpr (HM) {   // dims 16j + c16
+        if constexpr (!MF) {   // the lane groups' sums, then dims 8 c16 .. + 7 from lane group 0
 #pragma unroll
-            for (int j = 0; j < 8; ++j) sm.o[mb][slot][urow][16 * j + c16] = acc[j >> 2][j & 3];
-          } else {              // dims 8 c16 .. + 7
-            *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16]) = acc[0];
-            *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16 + 4]) = acc[1];
+          for (int i = 0; i < NACC; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = acc[i][e];
+              x += __shfl_xor(x, 16);
+              x += __shfl_xor(x, 32);
+              acc[i][e] = x;
+            }
           }
-        }
-      } else if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
-        if (own) {
+          if (grp == 0) {
+            if constexpr (HM) {   // dims 16j + c16
 #pragma unroll
-          for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][row][16 * i + 4 * grp]) = acc[i];
-        }
-      } else if (own) {     // MFMA i holds dims 32grp + 8r + i
-        float *dst = &sm.o[mb][slot][row][32 * grp];
+              for (int j = 0; j < 8; ++j) sm.o[mb][slot][urow][16 * j + c16] = acc[j >> 2][j & 3];
+            } else {              // dims 8 c16 .. + 7
+              *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16]) = acc[0];
+              *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][urow][8 * c16 + 4]) = acc[1];
+            }
+          }
+        } else if constexpr (HM) {   // MFMA i holds dims 16i + 4grp + r
+          if (own) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
-        }
-      }
-    };
-
-    auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
-      if constexpr (WIDE) {
-        if (i == cur.b1 || i == cur.b2 || i == cur.b3) {   // a phase of a wide item ends
-          store_state(mbuf, cur.ph0 + (i == cur.b1 ? 0 : i == cur.b2 ? 1 : 2) * cur.pst);
-          reset_state();
-        }
-      }
-      const int tok0 = tile_of<WIDE>(cur, i) << 4;
-      if constexpr (FUSE) {
-        if (i == new_i_cur) {
-          // the new token's place in the tile, and the load (lane group, instruction) of it
-          const int t = (cur.t1 - 1) & 15;
-          const int gn = BPT == 1 ? t >> 2 : (t % B) / RPI;
-          const int rn = BPT == 1 ? (t & 3) : (t / B) * RPI + (t % B) % RPI;
+            for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(&sm.o[mb][slot][row][16 * i + 4 * grp]) = acc[i];
+          }
+        } else if (own) {     // MFMA i holds dims 32grp + 8r + i
+          float *dst = &sm.o[mb][slot][row][32 * grp];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const bool mine = grp == gn && r == rn;
-            kr[r] = mine ? kn_cur : kr[r];
-            vr[r] = mine ? vn_cur : vr[r];
-          }
-          if (new_phys_cur >= 0 && grp == 0) {
-            const size_t off = ((size_t)new_phys_cur * B + (cur.t1 - 1) % B) * tsb + (size_t)cur.kvh * D * 2;
-            __builtin_amdgcn_raw_buffer_store_b128(kn_cur, buf_rsrc(kpool + off, D * 2), 16 * c16, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(vn_cur, buf_rsrc(vpool + off, D * 2), 16 * c16, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[8 * r + i] = acc[i][r];
           }
         }
-      }
-      if constexpr (!MF && HM) {
-        // head-major, one query head: lane (c16, grp) holds K chunks 4c + grp of tile row c16
-        // and the V pieces of rows 4grp .. 4grp + 3 at dims 16j + c16
-        float d = 0.f;
+      };
+
+      auto compute = [&](int i, u32x4 *kr, u32x4 *vr, u32x2 *vr2) {
+        if constexpr (WI) {
+          if (i == cur.b1 || i == cur.b2 || i == cur.b3) {   // a phase of a wide item ends
+            store_state(mbuf, cur.ph0 + (i == cur.b1 ? 0 : i == cur.b2 ? 1 : 2) * cur.pst);
+            reset_state();
+          }
+        }
+        const int tok0 = tile_of<WI>(cur, i) << 4;
+        if constexpr (FUSE) {
+          if (i == new_i_cur) {
+            // the new token's place in the tile, and the load (lane group, instruction) of it
+            const int t = (cur.t1 - 1) & 15;
+            const int gn = BPT == 1 ? t >> 2 : (t % B) / RPI;
+            const int rn = BPT == 1 ? (t & 3) : (t / B) * RPI + (t % B) % RPI;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+            for (int r = 0; r < 4; ++r) {
+              const bool mine = grp == gn && r == rn;
+              kr[r] = mine ? kn_cur : kr[r];
+              vr[r] = mine ? vn_cur : vr[r];
+            }
+            if (new_phys_cur >= 0 && grp == 0) {
+              const size_t off = ((size_t)new_phys_cur * B + (cur.t1 - 1) % B) * tsb + (size_t)cur.kvh * D * 2;
+              __builtin_amdgcn_raw_buffer_store_b128(kn_cur, buf_rsrc(kpool + off, D * 2), 16 * c16, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(vn_cur, buf_rsrc(vpool + off, D * 2), 16 * c16, 0, 0);
+            }
+          }
+        }
+        if constexpr (!MF && HM) {
+          // head-major, one query head: lane (c16, grp) holds K chunks 4c + grp of tile row c16
+          // and the V pieces of rows 4grp .. 4grp + 3 at dims 16j + c16
+          float d = 0.f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              d = __builtin_fmaf(bf16_lo(qop[c][w2]), bf16_lo(kr[c][w2]), d);
+              d = __builtin_fmaf(bf16_hi(qop[c][w2]), bf16_hi(kr[c][w2]), d);
+            }
+          }
+          d += __shfl_xor(d, 16);   // the four lane groups' 32 dims each
+          d += __shfl_xor(d, 32);
+          const int tk = tok0 + c16;
+          const float sv = tk >= cur.t0 && tk < cur.t1 ? d * a.scale_log2 : kNegInf;
+          const float mnew = fmaxf(m, group_max16(sv));
+          const float alpha = merge_weight(m, mnew);
+          const float pt = sv == kNegInf ? 0.f : fast_exp2(sv - mnew);
+          lsum = lsum * alpha + group_sum<16>(pt);   // the same in every lane
+          if (alpha != 1.f) {
+#pragma unroll
+            for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
+          }
+          m = mnew;
+          if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
+            uint32_t keep01 = 0u, keep23 = 0u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int tr = tok0 + 4 * grp + r;
+              const uint32_t half = tr >= cur.t0 && tr < cur.t1 ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
+              if (r < 2) keep01 |= half; else keep23 |= half;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
+          }
+          float pr[4];   // p of rows 4grp + r, held by lane 4grp + r
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] = __shfl(pt, 4 * grp + r);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t w = vr2[j][r >> 1];
+              acc[j >> 2][j & 3] = __builtin_fmaf(pr[r], (r & 1) ? bf16_hi(w) : bf16_lo(w), acc[j >> 2][j & 3]);
+            }
+          }
+          return;
+        }
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (!MF) {
+          // lane (c16, grp) holds dims 8 c16 .. + 7 of tile row 4 grp + r in kr[r]: a dot product
+          // over its 8 dims, then the sum over the 16 lanes of the row
+          float qf[8];
 #pragma unroll
           for (int w2 = 0; w2 < 4; ++w2) {
-            d = __builtin_fmaf(bf16_lo(qop[c][w2]), bf16_lo(kr[c][w2]), d);
-            d = __builtin_fmaf(bf16_hi(qop[c][w2]), bf16_hi(kr[c][w2]), d);
+            qf[2 * w2] = bf16_lo(qop[0][w2]);
+            qf[2 * w2 + 1] = bf16_hi(qop[0][w2]);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float d = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              d = __builtin_fmaf(qf[2 * w2], bf16_lo(kr[r][w2]), d);
+              d = __builtin_fmaf(qf[2 * w2 + 1], bf16_hi(kr[r][w2]), d);
+            }
+            sc[r] = group_sum<16>(d);
+          }
+        } else {
+          u32x4 kop[4];
+          if constexpr (HM) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kop[c] = kr[c];   // loaded in the A layout
+          } else {
+            // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t
+            // sits at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token,
+            // 16 chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of
+            // 64 banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 4 * grp + r;
+              kst[t * 16 + (c16 ^ t)] = kr[r];
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
+                                                         __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
+        }
+
+        // scores of tile rows 4grp + r (for head c16 on the MFMA path); positions outside
+        // [t0, t1) are masked
+        float sv[4], mx = kNegInf;
+        uint32_t keep01 = 0u, keep23 = 0u;   // head-major V: halves of the tokens in range
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tk = tok0 + (r / RPI) * B + RPI * grp + r % RPI;
+          const bool ok = tk >= cur.t0 && tk < cur.t1;
+          sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
+          if constexpr (HM) {
+            const uint32_t half = ok ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
+            if (r < 2) keep01 |= half; else keep23 |= half;
+          } else {
+            if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
+          }
+          mx = fmaxf(mx, sv[r]);
+        }
+        if constexpr (HM) {
+          if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
           }
         }
-        d += __shfl_xor(d, 16);   // the four lane groups' 32 dims each
-        d += __shfl_xor(d, 32);
-        const int tk = tok0 + c16;
-        const float sv = tk >= cur.t0 && tk < cur.t1 ? d * a.scale_log2 : kNegInf;
-        const float mnew = fmaxf(m, group_max16(sv));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m, mx);
         const float alpha = merge_weight(m, mnew);
-        const float pt = sv == kNegInf ? 0.f : fast_exp2(sv - mnew);
-        lsum = lsum * alpha + group_sum<16>(pt);   // the same in every lane
-        if (alpha != 1.f) {
+        float pr[4], ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr[r] = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - mnew);
+          ps += pr[r];
+        }
+        lsum = lsum * alpha + ps;
+        if (__any(alpha != 1.f)) {
 #pragma unroll
           for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
         }
         m = mnew;
-        if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
-          uint32_t keep01 = 0u, keep23 = 0u;
+
+        if constexpr (!MF) {
+          // P.V: each lane adds p(row) times its 8 dims of the row's V piece
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int tr = tok0 + 4 * grp + r;
-            const uint32_t half = tr >= cur.t0 && tr < cur.t1 ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
-            if (r < 2) keep01 |= half; else keep23 |= half;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+              acc[w2 >> 1][2 * (w2 & 1)] = __builtin_fmaf(pr[r], bf16_lo(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1)]);
+              acc[w2 >> 1][2 * (w2 & 1) + 1] =
+                  __builtin_fmaf(pr[r], bf16_hi(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1) + 1]);
+            }
           }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
+          return;
         }
-        float pr[4];   // p of rows 4grp + r, held by lane 4grp + r
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = __shfl(pt, 4 * grp + r);
+
+        const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
+        const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const uint32_t w = vr2[j][r >> 1];
-            acc[j >> 2][j & 3] = __builtin_fmaf(pr[r], (r & 1) ? bf16_hi(w) : bf16_lo(w), acc[j >> 2][j & 3]);
+          if constexpr (HM) {
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vr2[j]), pop, acc[j], 0, 0, 0);
+            continue;
           }
-        }
-        return;
-      }
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (!MF) {
-        // lane (c16, grp) holds dims 8 c16 .. + 7 of tile row 4 grp + r in kr[r]: a dot product
-        // over its 8 dims, then the sum over the 16 lanes of the row
-        float qf[8];
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          qf[2 * w2] = bf16_lo(qop[0][w2]);
-          qf[2 * w2 + 1] = bf16_hi(qop[0][w2]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float d = 0.f;
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            d = __builtin_fmaf(qf[2 * w2], bf16_lo(kr[r][w2]), d);
-            d = __builtin_fmaf(qf[2 * w2 + 1], bf16_hi(kr[r][w2]), d);
+          const int wd = j >> 1;
+          uint32_t a01, a23;
+          if (j & 1) {
+            a01 = (vr[0][wd] >> 16) | (vr[1][wd] & 0xffff0000u);
+            a23 = (vr[2][wd] >> 16) | (vr[3][wd] & 0xffff0000u);
+          } else {
+            a01 = (vr[0][wd] & 0xffffu) | (vr[1][wd] << 16);
+            a23 = (vr[2][wd] & 0xffffu) | (vr[3][wd] << 16);
           }
-          sc[r] = group_sum<16>(d);
-        }
-      } else {
-        u32x4 kop[4];
-        if constexpr (HM) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) kop[c] = kr[c];   // loaded in the A layout
-        } else {
-          // K tile to the MFMA A layout through the wave's LDS staging: chunk j of token t
-          // sits at t*16 + (j ^ t) (16-byte units), so both the row-wise writes (fixed token,
-          // 16 chunks) and the operand reads (16 tokens, fixed chunk) hit 16 distinct slots of
-          // 64 banks.  Lane (c16, grp) then holds token c16, chunks 4c + grp = dims 32c + 8grp ..
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 4 * grp + r;
-            kst[t * 16 + (c16 ^ t)] = kr[r];
-          }
-#pragma unroll
-          for (int c = 0; c < 4; ++c) kop[c] = kst[c16 * 16 + ((4 * c + grp) ^ c16)];
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[c]),
-                                                       __builtin_bit_cast(bf16x8, qop[c]), sc, 0, 0, 0);
-      }
-
-      // scores of tile rows 4grp + r (for head c16 on the MFMA path); positions outside
-      // [t0, t1) are masked
-      float sv[4], mx = kNegInf;
-      uint32_t keep01 = 0u, keep23 = 0u;   // head-major V: halves of the tokens in range
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tk = tok0 + (r / RPI) * B + RPI * grp + r % RPI;
-        const bool ok = tk >= cur.t0 && tk < cur.t1;
-        sv[r] = ok ? sc[r] * a.scale_log2 : kNegInf;
-        if constexpr (HM) {
-          const uint32_t half = ok ? ((r & 1) ? 0xffff0000u : 0xffffu) : 0u;
-          if (r < 2) keep01 |= half; else keep23 |= half;
-        } else {
-          if (!ok) vr[r] = (u32x4){0u, 0u, 0u, 0u};   // unread slots may hold anything
-        }
-        mx = fmaxf(mx, sv[r]);
-      }
-      if constexpr (HM) {
-        if (tok0 < cur.t0 || tok0 + 16 > cur.t1) {   // unread slots may hold anything
-#pragma unroll
-          for (int j = 0; j < 8; ++j) vr2[j] &= (u32x2){keep01, keep23};
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = merge_weight(m, mnew);
-      float pr[4], ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pr[r] = sv[r] == kNegInf ? 0.f : fast_exp2(sv[r] - mnew);
-        ps += pr[r];
-      }
-      lsum = lsum * alpha + ps;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int j = 0; j < NACC; ++j) acc[j] *= alpha;
-      }
-      m = mnew;
-
-      if constexpr (!MF) {
-        // P.V: each lane adds p(row) times its 8 dims of the row's V piece
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) {
-            acc[w2 >> 1][2 * (w2 & 1)] = __builtin_fmaf(pr[r], bf16_lo(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1)]);
-            acc[w2 >> 1][2 * (w2 & 1) + 1] =
-                __builtin_fmaf(pr[r], bf16_hi(vr[r][w2]), acc[w2 >> 1][2 * (w2 & 1) + 1]);
-          }
-        }
-        return;
-      }
-
-      const uint32_t p01 = pack_bf16x2(pr[0], pr[1]), p23 = pack_bf16x2(pr[2], pr[3]);
-      const i16x4 pop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){p01, p23});
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (HM) {
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vr2[j]), pop, acc[j], 0, 0, 0);
-          continue;
-        }
-        const int wd = j >> 1;
-        uint32_t a01, a23;
-        if (j & 1) {
-          a01 = (vr[0][wd] >> 16) | (vr[1][wd] & 0xffff0000u);
-          a23 = (vr[2][wd] >> 16) | (vr[3][wd] & 0xffff0000u);
-        } else {
-          a01 = (vr[0][wd] & 0xffffu) | (vr[1][wd] << 16);
-          a23 = (vr[2][wd] & 0xffffu) | (vr[3][wd] << 16);
-        }
-        const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[j], 0, 0, 0);
-      }
-    };
-
-    // the stream's first tiles
-    u32x4 kbuf[NB][4], vbuf[NB][4];
-    u32x2 vbuf2[NB][HM ? 8 : 1];   // head-major V pieces (unused on the row layout)
-    if constexpr (!kLate) {
-#pragma unroll
-      for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
-    }
-
-    for (int k = 0;; ++k) {
-      mbuf = k & 1;
-      if constexpr (kLate) {
-        // this item's first NB - 1 tiles (its table chunks and q were loaded when it was taken)
-#pragma unroll
-        for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
-      } else {
-        // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
-        // copies into the current item's registers at the end of this iteration, so those
-        // copies never wait on memory.
-        nxt = item_at<NB, WIDE>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
-        table_chunks<B, WIDE>(a, nxt, 0, lane, tb_next);
-        table_chunks<B, WIDE>(a, nxt, 1, lane, tb_next_ahead);
-        load_item_q(nxt, qnext);
-        load_item_new(nxt, kn_nxt, vn_nxt);
-        new_i_nxt = new_tile(nxt);
-        new_phys_nxt = -1;
-      }
-      // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
-      // of NB, so (two-ahead claims) the last NB - 1 steps issue the next item's tiles
-      // 0 .. NB-2 into buffers 0 .. NB-2; with kLate they issue nothing, and the next item's
-      // first tiles go out at the top of its own iteration.  That last body is a separate copy,
-      // so the wait on the next item's table entries sits only there.
-      // The first body is a copy of its own too: its waits count the loads and stores
-      // issued since this item's first tiles (the merge, the next item's table and q), so
-      // it does not wait for more tiles than the one it computes.
-      auto body = [&](int x) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          issue_cur(x + j + NB - 1, kbuf[(j + NB - 1) % NB], vbuf[(j + NB - 1) % NB], vbuf2[(j + NB - 1) % NB]);
-          __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
-          if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
+          const i16x4 aop = __builtin_bit_cast(i16x4, (uint32_t __attribute__((ext_vector_type(2)))){a01, a23});
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[j], 0, 0, 0);
         }
       };
-      int x = 0;
-      if (cur.n_pad > NB) {
-        body(0);
-        for (x = NB; x < cur.n_pad - NB; x += NB) body(x);
-      }
-      // Take the next item (kLate: it_{k+1}; else it_{k+2}) from the queue now, NB tiles
-      // before this item ends (its index is first read at the merge below).  Taking it later
-      // than at the item's start keeps a slow workgroup from claiming a long item early that a
-      // faster one would finish sooner.
-      const bool fetch = a.persistent && tid == 0 && (kLate || wn < total);
-      unsigned fetched = 0u;
-      if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
+
+      // the stream's first tiles
+      u32x4 kbuf[NB][4], vbuf[NB][4];
+      u32x2 vbuf2[NB][HM ? 8 : 1];   // head-major V pieces (unused on the row layout)
+      if constexpr (!kLate) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (j == 0)
-          issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1], vbuf2[NB - 1]);
-        else if constexpr (!kLate)
-          issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1], vbuf2[j - 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
+        for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
       }
 
-      // the waves' states of it_k into the merge buffer (the next item's first loads are in
-      // flight): the phase in progress, then empty states for a wide item's phases with no tiles
-      const int mb = k & 1;
-      if constexpr (WIDE) {
-        const int kcur = (cur.n_my > cur.b1) + (cur.n_my > cur.b2) + (cur.n_my > cur.b3);
-        store_state(mb, cur.ph0 + kcur * cur.pst);
-        for (int kk = kcur + 1; kk < cur.width; ++kk) {
-          reset_state();
-          store_state(mb, cur.ph0 + kk * cur.pst);
+      for (int k = 0;; ++k) {
+        mbuf = k & 1;
+        if constexpr (kLate) {
+          // this item's first NB - 1 tiles (its table chunks and q were loaded when it was taken)
+#pragma unroll
+          for (int j = 0; j < NB - 1; ++j) issue_cur(j, kbuf[j], vbuf[j], vbuf2[j]);
+        } else {
+          // The next item and its table chunks and q.  Loaded here, a whole tile loop before the
+          // copies into the current item's registers at the end of this iteration, so those
+          // copies never wait on memory.
+          nxt = item_at<NB, WI>(a, wn, sched, sm_pref, sm_ctx, sm_order, wave);
+          table_chunks<B, WI>(a, nxt, 0, lane, tb_next);
+          table_chunks<B, WI>(a, nxt, 1, lane, tb_next_ahead);
+          load_item_q(nxt, qnext);
+          load_item_new(nxt, kn_nxt, vn_nxt);
+          new_i_nxt = new_tile(nxt);
+          new_phys_nxt = -1;
         }
-      } else {
-        store_state(mb, wave);
-      }
-      if (lane == 0) sm.bad[mb][wave] = bad_cur;
-      if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)((kLate ? 1 : 2) * gridDim.x + fetched) : total;
-      __syncthreads();
-      if (cur.fill == 0)
-        tile_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
-      else if (cur.fill != 3)
-        fill_group<uint16_t, D>(a, cur.s, cur.kvh0 * a.g, cur.width * a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
-      if constexpr (kLate) {
-        // the item just taken: its table chunks, q and new rows
-        w = a.persistent ? sm.nextw[k & 1] : total;
-        if (w >= total) break;
-        cur = item_at<NB, WIDE>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
-        table_chunks<B, WIDE>(a, cur, 0, lane, tb_cur);
-        table_chunks<B, WIDE>(a, cur, 1, lane, tb_ahead);
-        load_item_q(cur, qop);
-        load_item_new(cur, kn_cur, vn_cur);
-        new_i_cur = new_tile(cur);
-        new_phys_cur = -1;
-        bad_cur = 0;
-        reset_state();
-        continue;
-      }
-      if (wn >= total) break;
+        // Step x computes tile x and issues stream position x + NB - 1.  n_pad is a multiple
+        // of NB, so (two-ahead claims) the last NB - 1 steps issue the next item's tiles
+        // 0 .. NB-2 into buffers 0 .. NB-2; with kLate they issue nothing, and the next item's
+        // first tiles go out at the top of its own iteration.  That last body is a separate copy,
+        // so the wait on the next item's table entries sits only there.
+        // The first body is a copy of its own too: its waits count the loads and stores
+        // issued since this item's first tiles (the merge, the next item's table and q), so
+        // it does not wait for more tiles than the one it computes.
+        auto body = [&](int x) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            issue_cur(x + j + NB - 1, kbuf[(j + NB - 1) % NB], vbuf[(j + NB - 1) % NB], vbuf2[(j + NB - 1) % NB]);
+            __builtin_amdgcn_sched_barrier(0);   // keep those loads ahead of this tile's wait
+            if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
+          }
+        };
+        int x = 0;
+        if (cur.n_pad > NB) {
+          body(0);
+          for (x = NB; x < cur.n_pad - NB; x += NB) body(x);
+        }
+        // Take the next item (kLate: it_{k+1}; else it_{k+2}) from the queue now, NB tiles
+        // before this item ends (its index is first read at the merge below).  Taking it later
+        // than at the item's start keeps a slow workgroup from claiming a long item early that a
+        // faster one would finish sooner.
+        const bool fetch = a.persistent && tid == 0 && (kLate || wn < total);
+        unsigned fetched = 0u;
+        if (fetch) fetched = atomicAdd(&a.queue[0], 1u);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (j == 0)
+            issue_cur(x + NB - 1, kbuf[NB - 1], vbuf[NB - 1], vbuf2[NB - 1]);
+          else if constexpr (!kLate)
+            issue_next(j - 1, tb_next, kbuf[j - 1], vbuf[j - 1], vbuf2[j - 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (x + j < cur.n_my) compute(x + j, kbuf[j], vbuf[j], vbuf2[j]);
+        }
 
-      // advance the stream by one item
-      w = wn;
-      wn = a.persistent ? sm.nextw[k & 1] : total;
-      cur = nxt;
-      kn_cur = kn_nxt;
-      vn_cur = vn_nxt;
-      new_i_cur = new_i_nxt;
-      new_phys_cur = new_phys_nxt;
+        // the waves' states of it_k into the merge buffer (the next item's first loads are in
+        // flight): the phase in progress, then empty states for a wide item's phases with no tiles
+        const int mb = k & 1;
+        if constexpr (WI) {
+          const int kcur = (cur.n_my > cur.b1) + (cur.n_my > cur.b2) + (cur.n_my > cur.b3);
+          store_state(mb, cur.ph0 + kcur * cur.pst);
+          for (int kk = kcur + 1; kk < cur.width; ++kk) {
+            reset_state();
+            store_state(mb, cur.ph0 + kk * cur.pst);
+          }
+        } else {
+          store_state(mb, wave);
+        }
+        if (lane == 0) sm.bad[mb][wave] = bad_cur;
+        if (tid == 0 && a.persistent) sm.nextw[k & 1] = fetch ? (int)((kLate ? 1 : 2) * gridDim.x + fetched) : total;
+        __syncthreads();
+        if (cur.fill == 0)
+          tile_finish(a, cur, sm.m[mb], sm.l[mb], sm.o[mb], sm.bad[mb]);
+        else if (cur.fill != 3)
+          fill_group<uint16_t, D>(a, cur.s, cur.kvh0 * a.g, cur.width * a.g, cur.fill == 1 ? 0.f : __builtin_nanf(""));
+        if constexpr (kLate) {
+          // the item just taken: its table chunks, q and new rows
+          w = a.persistent ? sm.nextw[k & 1] : total;
+          if (w >= total) break;
+          cur = item_at<NB, WI>(a, w, sched, sm_pref, sm_ctx, sm_order, wave);
+          table_chunks<B, WI>(a, cur, 0, lane, tb_cur);
+          table_chunks<B, WI>(a, cur, 1, lane, tb_ahead);
+          load_item_q(cur, qop);
+          load_item_new(cur, kn_cur, vn_cur);
+          new_i_cur = new_tile(cur);
+          new_phys_cur = -1;
+          bad_cur = 0;
+          reset_state();
+          continue;
+        }
+        if (wn >= total) break;
+
+        // advance the stream by one item
+        w = wn;
+        wn = a.persistent ? sm.nextw[k & 1] : total;
+        cur = nxt;
+        kn_cur = kn_nxt;
+        vn_cur = vn_nxt;
+        new_i_cur = new_i_nxt;
+        new_phys_cur = new_phys_nxt;
 #pragma unroll
-      for (int h = 0; h < BPT; ++h) {
-        tb_cur[h] = tb_next[h];
-        tb_ahead[h] = tb_next_ahead[h];
+        for (int h = 0; h < BPT; ++h) {
+          tb_cur[h] = tb_next[h];
+          tb_ahead[h] = tb_next_ahead[h];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
+        bad_cur = bad_next;
+        bad_next = 0;
+        m = kNegInf;
+        lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) qop[c] = qnext[c];
-      bad_cur = bad_next;
-      bad_next = 0;
-      m = kNegInf;
-      lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < NACC; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
+  };
+  if constexpr (WIDE) {
+    if (__builtin_amdgcn_readfirstlane(sched.nwide) > 0) run_items(std::true_type{});
+    else run_items(std::false_type{});
+  } else {
+    run_items(std::false_type{});
   }
   if (a.persistent) queue_done(a.queue);
 }
