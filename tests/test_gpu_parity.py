@@ -1005,6 +1005,25 @@ def test_wide_items_same_bits_full_size(monkeypatch, name, P, widths):
     H.check_close(got, ref, "bf16", f"{name} width {widths[-1]} P={P}")
 
 
+@pytest.mark.parametrize("name,P", [("mha7b", 0), ("long_splitk", 512)])
+def test_near_pool_one_head_loop_same_bits(monkeypatch, name, P):
+    # an identity-ordered pool (each sequence's blocks consecutive): the batch shape picks the
+    # wide-item kernel, whose sample then finds the blocks close together and runs the one-head
+    # item loop; the output is the one-head kernel's bit for bit and within the oracle's tolerance
+    wl = _wl(name)
+    wl.free_order = list(range(wl.num_blocks))
+    step = pbatch.step_for(wl)
+    assert np.all(np.diff(step.block_tables[0, :8]) == 1)
+    d = H.upload(wl, step)
+    H.gpu_step(wl, step, d, P, do_attn=False)
+    _say("near pool", name, "P", P)
+    base = _attend(monkeypatch, wl, step, d, P, 1)
+    got = _attend(monkeypatch, wl, step, d, P, None)
+    assert got.tobytes() == base.tobytes(), name
+    _, _, _, ref = H.oracle_step(wl, "steady", P)
+    H.check_close(got, ref, "bf16", f"{name} identity-ordered pool P={P}")
+
+
 WIDE_SHAPES = [
     # S, Hq, Hkv, B, ctx range, partition sizes
     (5, 8, 8, 16, (1, 700), (0, 64)),        # g = 1 (VALU dots)
