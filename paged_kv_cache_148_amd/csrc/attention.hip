@@ -10,12 +10,13 @@
 //
 // Work unit: one (KV head, context partition, sequence) item, processed by one
 // workgroup of 4 waves.  An item serves every query head of the KV head's group, so each
-// K/V byte is read once per group.  On the tile paths the bulk of a large launch goes out in
-// wide items of 2 or 4 adjacent KV heads of one (sequence, partition): the workgroup's waves
-// then read the same blocks at the same time (one address translation serves several waves,
-// which halves the translation misses of a pool scattered over gigabytes), and each head's
-// tiles are still accumulated and merged exactly as in a one-head item, so the width changes
-// no bit of the result.  Without a partition size the partition is the whole
+// K/V byte is read once per group.  On the tile paths, where the sequences' blocks lie far
+// apart in the pool, the bulk of a large launch goes out in wide items of 2 or 4 adjacent KV
+// heads of one (sequence, partition): the workgroup's waves then read the same blocks at the
+// same time (one address translation serves several waves, which cuts the translation misses
+// of a pool scattered over gigabytes more than threefold), and each head's tiles are still
+// accumulated and merged exactly as in a one-head item, so the width changes no bit of the
+// result.  Without a partition size the partition is the whole
 // context.  With one, an item leaves a partial state (running max m, sum l, unnormalised
 // o) as one contiguous record in the workspace and a second kernel merges the partials by
 // log-sum-exp;
