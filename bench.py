@@ -573,7 +573,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the decode path has no cross-GPU step in this build)", file=sys.stderr)
+              "(the decode path here has no cross-GPU step)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
