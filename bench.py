@@ -39,6 +39,7 @@ HBM_PEAK_GBS = 8000.0
 # recomputed for each step by batch.balanced_partition: the fork workload's 16 sequences x 8 KV
 # heads are half as many items as there are compute units)
 PARTITION = {"tiny_fp32": 0, "mha7b": 0, "gqa70b": 4096, "long_splitk": 512, "fork_cow": None}
+MAIN = "long_splitk"   # the line of record: the largest single-GPU workload
 
 
 def partition_for(name: str, cfg, step, num_cus: int = 256) -> int:
@@ -49,7 +50,6 @@ def partition_for(name: str, cfg, step, num_cus: int = 256) -> int:
         P = batch.balanced_partition(cfg.num_seqs, cfg.num_kv_heads, int(step.max_context_len), cfg.block_size,
                                      num_cus)
     return P
-MAIN = "long_splitk"
 
 
 def algorithmic_bytes(cfg, step) -> dict:
