@@ -81,9 +81,10 @@ constexpr size_t kQueueBytes = 256;     // work-queue header at the start of the
 constexpr int kWideMinItems = 4;
 constexpr int kWideReserve = 2;   // with items taken just in time 2 beat 0, 4 and 8 (mha7b, gqa70b)
 // ... and only where the sampled consecutive blocks of the sequences lie this far apart (in one
-// pool): on pools shuffled within windows of 32 MB one-head items were faster, within 256 MB and
-// beyond wide ones (long contexts, 512-token partitions).
-constexpr int64_t kWideFarBytes = 64ll << 20;
+// pool): on pools shuffled within windows of 2 MB one-head items were faster (by 3 us on the long
+// contexts' 512-token partitions), within windows of 32 MB and beyond wide ones (by 1-4 us on the
+// long contexts, gqa70b and mha7b at 32 MB, 11 us on the long contexts at 256 MB).
+constexpr int64_t kWideFarBytes = 4ll << 20;
 
 struct AttnArgs {
   void *out;
@@ -908,9 +909,9 @@ __global__ __launch_bounds__(kThreads) void attn_tile_kernel(const AttnArgs a) {
   // no queue fetch), then one index per queue fetch, counted from gridDim.x (kLate) or from
   // 2 * gridDim.x.  kLate: the fetch for it_{k+1} is made as it_k ends.  Otherwise the fetch for
   // it_{k+2} is made while it_k runs, so both the current and the next item are always known.
-  // Wide items pay where the sequences' blocks lie far apart (a pool scattered over hundreds of
-  // MB: address translation then bounds the stream); on a pool whose consecutive blocks lie close
-  // together one-head items stream faster.  Each wave samples 64 pairs of consecutive table
+  // Wide items pay where the sequences' blocks lie far apart (a pool scattered over tens of MB
+  // or more: address translation then weighs on the stream); on a pool whose consecutive blocks
+  // lie close together one-head items stream faster.  Each wave samples 64 pairs of consecutive table
   // entries (lane l: entries l / S and l / S + 1 of sequence l % S), loaded with the lengths
   // before the schedule build, and the launch goes wide where most sampled pairs of blocks
   // that a sequence uses lie at least far_blocks apart (every workgroup sees the same bits).
