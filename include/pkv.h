@@ -30,10 +30,11 @@
  * host; how each kernel treats out-of-range device values is stated per call.
  *
  * Supported shapes: head_dim in {64, 128}; block_size in {4, 8, 16, 32, 64, 128};
- * num_heads % num_kv_heads == 0; dtype fp32 or bf16.  Attention runs on the bf16
- * matrix-core path for head_dim 128 and block_size >= 16 (g = num_heads /
- * num_kv_heads <= 16), otherwise on the vector path, which needs block_size <= 32
- * and g <= 8.  pkv_attention_path reports which.
+ * num_heads % num_kv_heads == 0; dtype fp32 or bf16.  bf16 attention with head_dim
+ * 128 and g = num_heads / num_kv_heads <= 16 runs on the tile path, at every block
+ * size (matrix cores for g >= 2, fp32 vector dot products for g = 1); everything else
+ * runs on the vector path, which needs block_size <= 32 and g <= 8.
+ * pkv_attention_path reports which.
  * All data pointers must be 16-byte aligned, index arrays 4- or 8-byte aligned.
  */
 #ifndef PKV_H
