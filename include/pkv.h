@@ -176,7 +176,7 @@ pkv_status copy_blocks(void *k_cache, void *v_cache, const int64_t *block_mappin
  * table).  Outputs and caches are bit-identical to those two calls.  On the tile paths
  * (PKV_PATH_MFMA, PKV_PATH_TILE_VALU) the row of each sequence's new token is written by the
  * work item that attends to it and used from registers, in the one launch; where the MFMA
- * tiles split into partitions of at most 512 tokens, and on the vector path, the write is a
+ * tiles split into partitions of at most 256 tokens, and on the vector path, the write is a
  * launch of its own just before the attention's.
  *
  * Arguments as for paged_attention_decode, plus k_new and v_new (device, 16-byte aligned;
