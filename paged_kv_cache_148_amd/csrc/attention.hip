@@ -1827,11 +1827,13 @@ __global__ __launch_bounds__(kMergeThreads) void attn_reduce_kernel(const AttnAr
 // Pass 2 for at most kShortParts partials per head (the partition count is bounded by the
 // host): a workgroup merges kReduceHeads heads of one sequence, a lane per 16-byte chunk of
 // a head's output, with every (m, l) pair and partial of the lane loaded at once -- two
-// dependent rounds of loads (the length, then the records) per workgroup, and a sixteenth of
-// the workgroups of one per (sequence, head).  The maximum first, then the weighted sums, in
-// ascending partition order.
+// dependent rounds of loads (the length, then the records) per workgroup.  With 8 heads (at
+// head_dim 128) every wave takes two heads in one pass; 16 or more heads per workgroup, in
+// passes one after the other, and 4, with waves left idle, were slower (gqa70b at 4096-token
+// partitions 268.5 / 266.7 / 267.1 us for 16 / 8 / 4, fork_cow steady 25.0 / 23.8 / 23.6 us).
+// The maximum first, then the weighted sums, in ascending partition order.
 constexpr int kShortParts = 16;
-constexpr int kReduceHeads = 16;
+constexpr int kReduceHeads = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void attn_reduce_short_kernel(const AttnArgs a) {
   constexpr int CH = D / 4;      // 16-byte chunks of fp32 per head: 32 or 16
