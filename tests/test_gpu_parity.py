@@ -1005,23 +1005,33 @@ def test_wide_items_same_bits_full_size(monkeypatch, name, P, widths):
     H.check_close(got, ref, "bf16", f"{name} width {widths[-1]} P={P}")
 
 
-@pytest.mark.parametrize("name,P", [("mha7b", 0), ("long_splitk", 512)])
-def test_near_pool_one_head_loop_same_bits(monkeypatch, name, P):
-    # an identity-ordered pool (each sequence's blocks consecutive): the batch shape picks the
-    # wide-item kernel, whose sample then finds the blocks close together and runs the one-head
-    # item loop; the output is the one-head kernel's bit for bit and within the oracle's tolerance
+@pytest.mark.parametrize("name,P,window", [("mha7b", 0, None), ("long_splitk", 512, None), ("long_splitk", 512, 64),
+                                           ("long_splitk", 512, 1024)])
+def test_near_pool_one_head_loop_same_bits(monkeypatch, name, P, window):
+    # an identity-ordered pool (each sequence's blocks consecutive; window None) or one shuffled
+    # only within windows of `window` block ids (2 MB or 32 MB of 32 KB blocks): the batch shape
+    # picks the wide-item kernel, whose sample finds the blocks close together (identity, 2 MB:
+    # the one-head item loop) or far enough apart (32 MB: wide items); either way the output is
+    # the one-head kernel's bit for bit and within the oracle's tolerance
     wl = _wl(name)
-    wl.free_order = list(range(wl.num_blocks))
+    ids = np.arange(wl.num_blocks)
+    if window is not None:
+        rng = np.random.default_rng(7)
+        for i in range(0, wl.num_blocks, window):
+            ids[i:i + window] = rng.permutation(ids[i:i + window])
+        ids = ids[::-1]
+    wl.free_order = [int(x) for x in ids]
     step = pbatch.step_for(wl)
-    assert np.all(np.diff(step.block_tables[0, :8]) == 1)
+    if window is None:
+        assert np.all(np.diff(step.block_tables[0, :8]) == 1)
     d = H.upload(wl, step)
     H.gpu_step(wl, step, d, P, do_attn=False)
-    _say("near pool", name, "P", P)
+    _say("near pool", name, "P", P, "window", window)
     base = _attend(monkeypatch, wl, step, d, P, 1)
     got = _attend(monkeypatch, wl, step, d, P, None)
     assert got.tobytes() == base.tobytes(), name
     _, _, _, ref = H.oracle_step(wl, "steady", P)
-    H.check_close(got, ref, "bf16", f"{name} identity-ordered pool P={P}")
+    H.check_close(got, ref, "bf16", f"{name} pool window {window} P={P}")
 
 
 WIDE_SHAPES = [
